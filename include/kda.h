@@ -1,0 +1,129 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The operation (page "Notations mathematiques", table "Attention et KDA"):
+ * per sequence and head, a state S in R^{d_k x d_v} evolves token by token as
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     alpha_t = exp(g_t)           (per-key-channel retention, row "alpha_t"),
+ *     o_t     = S_t^T q_t          (raw output before the output gate, row "o~_t").
+ * q_t and k_t are expected L2-normalised (rows q_t, k_t), g_t in [g_min, 0] with
+ * g_min = -5 (rows g_t, g_min) and beta_t in [0, 1] (row beta_t).
+ *
+ * kda_chunk_fwd evaluates this recurrence for prefill with the chunkwise form
+ * ("Glossaire", entry "Chunkwise": serial across blocks, parallel inside a
+ * block, exact), block size C from table "Dimensions du modele", row C (64 or
+ * 128).  kda_step_decode advances every request by one token ("Glossaire",
+ * entry "Decode").
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense, row-major (last index fastest), token-major and
+ *     packed: q, k, g are [total_tokens][H][d_k]; v, o are [total_tokens][H][d_v];
+ *     beta is [total_tokens][H]; states are [num_seqs][H][d_k][d_v].
+ *   - q, k, v and o share one element type (kda_dtype): fp32 or bf16.  g, beta
+ *     and every state are always fp32.
+ *   - Every pointer except the host-side sizes is a DEVICE pointer and must be
+ *     16-byte aligned.
+ *   - Supported sizes: d_k == d_v in {32, 64, 128}; chunk_size in {64, 128}.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises: work is enqueued on `stream` and the call returns at once.
+ *     Buffers must stay alive until the stream has passed the work.
+ *   - Arguments are validated on the host before any HIP call; an invalid call
+ *     returns a status and enqueues nothing.  A launch failure returns
+ *     KDA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.  Input value ranges (normalised keys, g and beta ranges,
+ *     monotone cu_seqlens) are preconditions and are not checked on the device.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* element type of q, k, v and o */
+typedef int32_t kda_dtype;
+#define KDA_F32 0
+#define KDA_BF16 1
+
+/* status codes */
+typedef int32_t kda_status;
+#define KDA_OK 0
+#define KDA_ERR_NULL 1        /* a required pointer is NULL                     */
+#define KDA_ERR_SHAPE 2       /* negative or inconsistent sizes                 */
+#define KDA_ERR_UNSUPPORTED 3 /* head size, chunk size or dtype not supported   */
+#define KDA_ERR_ALIGN 4       /* a pointer is not 16-byte aligned               */
+#define KDA_ERR_WORKSPACE 5   /* workspace smaller than the size asked for      */
+#define KDA_ERR_HIP 6         /* the HIP runtime reported an error at launch    */
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 means the
+ * workspace pointer may be NULL).  Pure host function.
+ */
+size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                    int32_t d_k, int32_t d_v, int32_t chunk_size,
+                                    kda_dtype dtype);
+
+/*
+ * Chunkwise prefill over packed variable-length sequences.
+ *
+ *   q, k          [total_tokens][H][d_k]  dtype         queries, keys (L2-normalised)
+ *   v             [total_tokens][H][d_v]  dtype         values
+ *   g             [total_tokens][H][d_k]  fp32          log-decay, alpha = exp(g)
+ *   beta          [total_tokens][H]       fp32          write strength
+ *   initial_state [num_seqs][H][d_k][d_v] fp32 or NULL  state entering each
+ *                                                       sequence (NULL = zeros,
+ *                                                       the S~ convention of the
+ *                                                       notation table)
+ *   cu_seqlens    [num_seqs + 1] int32 (device) or NULL.  Sequence n covers
+ *                 tokens [cu[n], cu[n+1]); cu[0] = 0, non-decreasing,
+ *                 cu[num_seqs] = total_tokens; zero-length sequences are allowed
+ *                 (their final state is their initial state).  NULL means
+ *                 num_seqs sequences of equal length total_tokens / num_seqs
+ *                 (total_tokens must then be a multiple of num_seqs).
+ *                 The host never reads cu_seqlens.
+ *   chunk_size    64 or 128; the result does not depend on it beyond rounding.
+ *   o             [total_tokens][H][d_v]  dtype         o_t = S_t^T q_t; must not
+ *                                                       alias an input
+ *   final_state   [num_seqs][H][d_k][d_v] fp32 or NULL  state after each sequence;
+ *                                                       may alias initial_state
+ *   workspace     device scratch of at least kda_chunk_fwd_workspace_size(...)
+ *                 bytes (may be NULL when that size is 0).
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         int32_t H, int32_t d_k, int32_t d_v, int32_t chunk_size,
+                         kda_dtype dtype, void *o, float *final_state, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step: each of N requests appends one token and advances its own
+ * state in place ("Glossaire", entry "Decode": bandwidth bound).
+ *
+ *   q, k   [N][H][d_k] dtype;  v [N][H][d_v] dtype;  g [N][H][d_k] fp32;
+ *   beta   [N][H] fp32;
+ *   state  [N][H][d_k][d_v] fp32, read and overwritten with S_t;
+ *   o      [N][H][d_v] dtype, o_t = S_t^T q_t; must not alias any input.
+ */
+kda_status kda_step_decode(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, void *o, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *kda_status_string(kda_status status);
+
+/* KDA_ABI_VERSION of the built library. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

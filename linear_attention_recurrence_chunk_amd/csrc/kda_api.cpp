@@ -1,0 +1,118 @@
+// C ABI of libkda.so: argument validation (host only, before any HIP call),
+// dispatch to the gfx950 kernels, and launch-error mapping.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+hipError_t launch_prefill(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *s0, const int32_t *cu, int num_seqs,
+                          int64_t seq_len, int H, int d, int chunk, bool is_bf16, void *o,
+                          float *sf, hipStream_t stream);
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *state, void *o, int64_t NH, int d,
+                         bool is_bf16, hipStream_t stream);
+}  // namespace kda
+
+namespace {
+
+bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool head_size_ok(int32_t d, kda_dtype dt, bool prefill)
+{
+    if (dt == KDA_BF16) return d == 32 || d == 64 || d == 128;
+    if (dt == KDA_F32) return prefill ? (d == 32 || d == 64) : (d == 32 || d == 64 || d == 128);
+    return false;
+}
+
+bool chunk_ok(int32_t c) { return c == 64; }
+
+kda_status prefill_check(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *s0, const int32_t *cu,
+                         int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
+                         int32_t d_v, int32_t chunk, kda_dtype dt, const void *o,
+                         const float *sf, const void *ws, size_t ws_bytes)
+{
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || total_tokens < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
+    if (d_k != d_v || !head_size_ok(d_k, dt, true)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 64 && chunk != 128) return KDA_ERR_UNSUPPORTED;
+    if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_SHAPE;
+    if (!cu && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_SHAPE;
+    if ((int64_t)num_seqs * H * 2 > INT32_MAX) return KDA_ERR_SHAPE;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
+        misaligned(s0) || misaligned(cu) || misaligned(o) || misaligned(sf) || misaligned(ws))
+        return KDA_ERR_ALIGN;
+    const size_t need =
+        kda_chunk_fwd_workspace_size(num_seqs, total_tokens, H, d_k, d_v, chunk, dt);
+    if (ws_bytes < need || (need > 0 && !ws)) return KDA_ERR_WORKSPACE;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_fwd_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t, int32_t,
+                                    kda_dtype)
+{
+    return 0;  // the fused kernel keeps every intermediate on chip
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         int32_t H, int32_t d_k, int32_t d_v, int32_t chunk_size,
+                         kda_dtype dtype, void *o, float *final_state, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream)
+{
+    const kda_status st =
+        prefill_check(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, H,
+                      d_k, d_v, chunk_size, dtype, o, final_state, workspace, workspace_bytes);
+    if (st != KDA_OK) return st;
+    if (num_seqs == 0) return KDA_OK;
+    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
+    const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, cu_seqlens,
+                                             num_seqs, seq_len, H, d_k, chunk_size,
+                                             dtype == KDA_BF16, o, final_state, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_step_decode(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, void *o, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
+    if (d_k != d_v || !head_size_ok(d_k, dtype, false)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
+        misaligned(state) || misaligned(o))
+        return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_decode(q, k, v, g, beta, state, o, (int64_t)N * H, d_k,
+                                            dtype == KDA_BF16, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const char *kda_status_string(kda_status s)
+{
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "negative or inconsistent sizes";
+        case KDA_ERR_UNSUPPORTED: return "head size, chunk size or dtype not supported";
+        case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case KDA_ERR_WORKSPACE: return "workspace smaller than kda_chunk_fwd_workspace_size";
+        case KDA_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int32_t kda_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

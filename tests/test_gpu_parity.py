@@ -1,0 +1,196 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: bf16 inputs  max|x - x_ref| <= 2e-2 * max|x_ref|, for o and for the
+final state; fp32 inputs 1e-4 on the same measure.  Full-size workloads are
+checked on sampled heads (every token of those heads, every sequence), which
+the oracle computes one (sequence, head) at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_chunk_amd import inputs
+from linear_attention_recurrence_chunk_amd import _lib as kda
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+def rel_err(x, ref) -> float:
+    x = x.detach().double().cpu().numpy() if hasattr(x, "detach") else np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    assert np.isfinite(x).all(), "non-finite output"
+    return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def report(name, **errs):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+
+
+def run_prefill(x, chunk, heads=None):
+    """GPU on the whole input; oracle on `heads` (all when None).  Returns errors."""
+    o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                          x["cu_seqlens"], chunk_size=chunk)
+    torch.cuda.synchronize()
+    hs = slice(None) if heads is None else list(heads)
+    sub = lambda t: None if t is None else t[:, hs].cpu()
+    o_ref, sf_ref = oracle.forward(sub(x["q"]), sub(x["k"]), sub(x["v"]), sub(x["g"]),
+                                   sub(x["beta"]), sub(x["initial_state"]),
+                                   x["cu_seqlens"].cpu().numpy())
+    return rel_err(o[:, hs], o_ref), rel_err(sf[:, hs], sf_ref)
+
+
+# ---------------------------------------------------------------------------
+# decode
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_decode_small(dtype, d):
+    w = inputs.custom(H=3, dk=d, dv=d, dtype=dtype, decode_requests=5, state_std=0.5)
+    x = inputs.decode_inputs(w, seed=d, device=DEV)
+    st0 = x["state"].clone()
+    o = kda.step_decode(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"])
+    torch.cuda.synchronize()
+    o_ref, st_ref = oracle.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], st0)
+    eo, es = rel_err(o, o_ref), rel_err(x["state"], st_ref)
+    report(f"decode d={d} {dtype}", o=eo, state=es)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_decode_k3_256_requests():
+    w = inputs.WORKLOADS["k3_decode_256"]
+    x = inputs.decode_inputs(w, seed=5, device=DEV)
+    st0 = x["state"].cpu()
+    o = kda.step_decode(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"])
+    torch.cuda.synchronize()
+    o_ref, st_ref = oracle.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], st0)
+    eo, es = rel_err(o, o_ref), rel_err(x["state"], st_ref)
+    report("decode k3 N=256", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# prefill, small shapes (whole oracle)
+def test_prefill_tiny_fp32():
+    w = inputs.WORKLOADS["tiny_fp32"]
+    x = inputs.prefill_inputs(w, seed=1, device=DEV)
+    eo, es = run_prefill(x, w.chunk)
+    report("prefill tiny fp32", o=eo, state=es)
+    assert eo <= 1e-4 and es <= 1e-4
+
+
+CASES = [
+    # (dtype, d, seqlens, H, state_std)
+    (torch.bfloat16, 128, [300], 4, 0.0),
+    (torch.bfloat16, 128, [64, 1, 0, 129, 200], 3, 0.05),
+    (torch.bfloat16, 64, [250, 63], 4, 0.05),
+    (torch.bfloat16, 32, [333], 2, 0.0),
+    (torch.float32, 32, [100, 0, 77, 256], 2, 0.1),
+    (torch.float32, 64, [190], 2, 0.1),
+]
+
+
+@pytest.mark.parametrize("dtype,d,lens,H,std", CASES)
+def test_prefill_shapes(dtype, d, lens, H, std):
+    w = inputs.custom(H=H, dk=d, dv=d, seqlens=lens, dtype=dtype, state_std=std)
+    x = inputs.prefill_inputs(w, seed=sum(lens) + d, device=DEV)
+    eo, es = run_prefill(x, 64)
+    report(f"prefill {dtype} d={d} lens={lens}", o=eo, state=es)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("gate", ["no_decay", "max_decay"])
+@pytest.mark.parametrize("bval", [0.0, 1.0])
+def test_prefill_degenerate_gates(gate, bval):
+    """g = 0 (alpha = 1) or g = g_min everywhere; beta all 0 or all 1."""
+    w = inputs.custom(H=2, dk=128, dv=128, seqlens=[150, 40], state_std=0.1)
+    x = inputs.prefill_inputs(w, seed=7, device=DEV)
+    x["g"].fill_(0.0 if gate == "no_decay" else -5.0)
+    x["beta"].fill_(bval)
+    eo, es = run_prefill(x, 64)
+    report(f"prefill gate={gate} beta={bval}", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled heads
+def test_prefill_k3_8k():
+    w = inputs.WORKLOADS["k3_prefill_8k"]
+    x = inputs.prefill_inputs(w, seed=2, device=DEV)
+    eo, es = run_prefill(x, w.chunk, heads=[0, 31, 64, 95])
+    report("prefill k3 8k", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_prefill_varlen_prefix():
+    w = inputs.WORKLOADS["k3_varlen_prefix"]
+    x = inputs.prefill_inputs(w, seed=4, device=DEV)
+    print(f"[parity] varlen lengths {x['seqlens']}", flush=True)
+    eo, es = run_prefill(x, w.chunk, heads=[0, 47, 48, 95])
+    report("prefill varlen+prefix", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# self-consistency of the HIP path
+def test_prefill_equals_repeated_decode():
+    w = inputs.custom(H=3, dk=128, dv=128, seqlens=[70], state_std=0.1)
+    x = inputs.prefill_inputs(w, seed=11, device=DEV)
+    o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                          x["cu_seqlens"])
+    st = x["initial_state"].clone()
+    outs = []
+    for t in range(70):
+        sl = slice(t, t + 1)
+        outs.append(kda.step_decode(x["q"][sl], x["k"][sl], x["v"][sl], x["g"][sl],
+                                    x["beta"][sl], st))
+    torch.cuda.synchronize()
+    od = torch.cat(outs)
+    e1 = rel_err(o, od.double().cpu().numpy())
+    e2 = rel_err(sf, st.double().cpu().numpy())
+    report("prefill vs repeated decode", o=e1, state=e2)
+    assert e1 <= 2e-2 and e2 <= 2e-2
+
+
+def test_prefill_split_resume_equals_whole():
+    w = inputs.custom(H=4, dk=128, dv=128, seqlens=[500], state_std=0.05)
+    x = inputs.prefill_inputs(w, seed=12, device=DEV)
+    o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"])
+    cut = 200
+    a = lambda t: t[:cut].contiguous()
+    b = lambda t: t[cut:].contiguous()
+    o1, s1 = kda.chunk_fwd(a(x["q"]), a(x["k"]), a(x["v"]), a(x["g"]), a(x["beta"]),
+                           x["initial_state"])
+    o2, s2 = kda.chunk_fwd(b(x["q"]), b(x["k"]), b(x["v"]), b(x["g"]), b(x["beta"]), s1)
+    torch.cuda.synchronize()
+    e1 = rel_err(torch.cat([o1, o2]), o.double().cpu().numpy())
+    e2 = rel_err(s2, sf.double().cpu().numpy())
+    report("split/resume", o=e1, state=e2)
+    assert e1 <= 2e-2 and e2 <= 2e-2
+
+
+def test_prefill_is_deterministic_and_final_may_alias_initial():
+    w = inputs.custom(H=8, dk=128, dv=128, seqlens=[1000, 333], state_std=0.05)
+    x = inputs.prefill_inputs(w, seed=13, device=DEV)
+    o1, s1 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                           x["cu_seqlens"])
+    o2, s2 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                           x["cu_seqlens"])
+    inplace = x["initial_state"].clone()
+    o3, s3 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], inplace,
+                           x["cu_seqlens"], final_state=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(o1, o3) and torch.equal(s1, inplace)
+
+
+def test_decode_is_deterministic():
+    w = inputs.WORKLOADS["k3_decode_256"]
+    x = inputs.decode_inputs(w, seed=21, device=DEV, requests=8)
+    s_a, s_b = x["state"].clone(), x["state"].clone()
+    o_a = kda.step_decode(x["q"], x["k"], x["v"], x["g"], x["beta"], s_a)
+    o_b = kda.step_decode(x["q"], x["k"], x["v"], x["g"], x["beta"], s_b)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(s_a, s_b)
