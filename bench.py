@@ -1,0 +1,216 @@
+"""Benchmark of the chunkwise KDA prefill (and the decode step) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one kda_chunk_fwd over the whole workload (default: one sequence of
+8192 tokens, H = 96, d_k = d_v = 128, C = 64, bf16 q/k/v, fp32 g/beta), with
+every input already resident in HBM.  The decode step (256 requests, H = 96,
+fp32 states updated in place) is timed after it and reported under "decode".
+Rank 0 prints one JSON line.
+
+Roofline figures (per launch):
+  prefill bytes  B_alg = N_tok H [e_in (2 d_k + d_v) + 4 d_k + 4 + e_out d_v]
+                         + N_seq H d_k d_v 4 (has_initial + has_final)
+  prefill flops  F     = N_tok H [C (3 d_k + 2 d_v) + 6 d_k d_v]
+                 (K K^T, Q K^T, T R, P U at C^2 d / 2 each, triangle-aware, and
+                  K e^G S, Q e^G S, Kbar^T U at 2 C d_k d_v / C each per token)
+  decode bytes   N H [8 d_k d_v + e_in (2 d_k + d_v) + 4 d_k + 4 + e_out d_v]
+The prefill at these shapes is bound by HBM (90 flop per byte, below the
+bf16 ridge of 2.5e15 / 8e12 = 312), so the roofline object uses HBM bandwidth;
+the matrix-core fraction is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+METRIC = "KDA prefill tokens/s (H=96, d_k=d_v=128) + % bf16 MFMA peak; decode HBM GB/s"
+
+
+def prefill_bytes(n_tok, n_seq, H, dk, dv, e_in, e_out, has_s0, has_sf):
+    return (n_tok * H * (e_in * (2 * dk + dv) + 4 * dk + 4 + e_out * dv)
+            + n_seq * H * dk * dv * 4 * (int(has_s0) + int(has_sf)))
+
+
+def prefill_flops(n_tok, H, dk, dv, C):
+    return n_tok * H * (C * (3 * dk + 2 * dv) + 6 * dk * dv)
+
+
+def decode_bytes(N, H, dk, dv, e_in, e_out):
+    return N * H * (8 * dk * dv + e_in * (2 * dk + dv) + 4 * dk + 4 + e_out * dv)
+
+
+def _source_sha(name):
+    p = os.path.join(ROOT, "linear_attention_recurrence_chunk_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel_file, workload):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    measurement was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != _source_sha(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Average duration of `fn` (one launch) with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def cpu_baseline(x, w, budget_heads=None):
+    """The fp64 oracle on a bounded sample of the workload: every token of a
+    subset of heads, threaded over heads on all host cores."""
+    import oracle
+    cores = oracle.default_threads()
+    h = budget_heads or min(w.H, 4 * cores)
+    heads = list(range(h))
+    sub = {n: x[n][:, heads].cpu() for n in ("q", "k", "v", "g", "beta")}
+    s0 = None if x["initial_state"] is None else x["initial_state"][:, heads].cpu()
+    cu = x["cu_seqlens"].cpu().numpy()
+    n_tok = int(cu[-1])
+    t0 = time.perf_counter()
+    oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], s0, cu, nthreads=cores)
+    dt = time.perf_counter() - t0
+    # full-workload tokens per second (a token carries all H heads)
+    return {"value": n_tok * h / w.H / dt, "unit": "tokens/s", "cores": min(cores, h * (len(cu) - 1)),
+            "kind": "oracle",
+            "sample": f"{h} of {w.H} heads x all {n_tok} tokens of {w.name} (fp64, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="k3_prefill_8k")
+    ap.add_argument("--decode-workload", default="k3_decode_256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (to scale HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from linear_attention_recurrence_chunk_amd import _lib as kda
+    from linear_attention_recurrence_chunk_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.library()                                  # fails loudly if not built
+
+    # ---- prefill
+    w = inputs.WORKLOADS[args.workload]
+    x = inputs.prefill_inputs(w, seed=2, device=dev)
+    n_tok, n_seq = int(x["q"].shape[0]), len(x["seqlens"])
+    o = torch.empty_like(x["v"])
+    sf = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                      x["cu_seqlens"], chunk_size=w.chunk, out=o, final_state=sf)
+
+    ms, wall = time_launches(step, args.steps, args.warmup, torch)
+    e = x["q"].element_size()
+    bytes_ = prefill_bytes(n_tok, n_seq, w.H, w.dk, w.dv, e, e,
+                           x["initial_state"] is not None, True)
+    flops = prefill_flops(n_tok, w.H, w.dk, w.dv, w.chunk)
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    toks = n_tok / (ms * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": toks,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if x["q"].dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": n_seq, "tokens": n_tok, "H": w.H,
+                   "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk,
+                   "initial_state": x["initial_state"] is not None,
+                   "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": _traffic("kda_prefill.hip", w.name),
+                     "kernel": "kda::prefill_kernel", "bytes_per_launch": bytes_},
+        "mfma": {"tflops": tflops, "peak": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
+                 "flops_per_launch": flops},
+        "wall_s_timed": wall,
+    }
+
+    # ---- decode
+    if not args.no_decode:
+        wd = inputs.WORKLOADS[args.decode_workload]
+        xd = inputs.decode_inputs(wd, seed=5, device=dev)
+        od = torch.empty_like(xd["v"])
+
+        def dstep():
+            kda.step_decode(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["state"], out=od)
+
+        dms, _ = time_launches(dstep, args.steps, args.warmup, torch)
+        ed = xd["q"].element_size()
+        dbytes = decode_bytes(wd.decode_requests, wd.H, wd.dk, wd.dv, ed, ed)
+        dgbs = dbytes / (dms * 1e-3) / 1e9
+        out["decode"] = {"workload": wd.name, "requests": wd.decode_requests, "ms_per_step": dms,
+                         "GB/s": dgbs, "roofline": {"bound": "hbm", "achieved": dgbs,
+                                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                    "frac": dgbs / HBM_PEAK_GBS,
+                                                    "traffic": _traffic("kda_decode.hip", wd.name),
+                                                    "kernel": "kda::decode_kernel",
+                                                    "bytes_per_launch": dbytes}}
+        del xd
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": src.numel() * 4}
+        del src, dst
+
+    # ---- oracle on the host cores (context only)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

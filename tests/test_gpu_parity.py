@@ -143,9 +143,8 @@ def test_prefill_equals_repeated_decode():
     st = x["initial_state"].clone()
     outs = []
     for t in range(70):
-        sl = slice(t, t + 1)
-        outs.append(kda.step_decode(x["q"][sl], x["k"][sl], x["v"][sl], x["g"][sl],
-                                    x["beta"][sl], st))
+        one = [x[n][t:t + 1].clone() for n in ("q", "k", "v", "g", "beta")]  # 16-byte aligned
+        outs.append(kda.step_decode(*one, st))
     torch.cuda.synchronize()
     od = torch.cat(outs)
     e1 = rel_err(o, od.double().cpu().numpy())
