@@ -23,7 +23,8 @@
  *     and every state are always fp32.
  *   - Every pointer except the host-side sizes is a DEVICE pointer and must be
  *     16-byte aligned.
- *   - Supported sizes: d_k == d_v in {32, 64, 128}; chunk_size in {64, 128}.
+ *   - Supported sizes: d_k == d_v in {32, 64, 128} (bf16) or {32, 64} (fp32
+ *     prefill; decode takes all three); chunk_size in {64, 128}.
  *   - The caller owns every buffer.  The library never allocates, frees or
  *     synchronises: work is enqueued on `stream` and the call returns at once.
  *     Buffers must stay alive until the stream has passed the work.
@@ -88,7 +89,9 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  *                 num_seqs sequences of equal length total_tokens / num_seqs
  *                 (total_tokens must then be a multiple of num_seqs).
  *                 The host never reads cu_seqlens.
- *   chunk_size    64 or 128; the result does not depend on it beyond rounding.
+ *   chunk_size    64 or 128 (table "Dimensions du modele", row C).  The chunkwise
+ *                 form is exact for any block size; this implementation advances
+ *                 the state every 64 tokens for both values.
  *   o             [total_tokens][H][d_v]  dtype         o_t = S_t^T q_t; must not
  *                                                       alias an input
  *   final_state   [num_seqs][H][d_k][d_v] fp32 or NULL  state after each sequence;

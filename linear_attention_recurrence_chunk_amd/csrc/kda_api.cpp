@@ -26,7 +26,11 @@ bool head_size_ok(int32_t d, kda_dtype dt, bool prefill)
     return false;
 }
 
-bool chunk_ok(int32_t c) { return c == 64; }
+// Both block sizes of the notation table are accepted.  The kernel advances
+// the state every 64 tokens for either value: the chunkwise form is exact for
+// any block size, so the result is the same up to rounding, and on this
+// design a 128-token intra-chunk block only adds work per token.
+bool chunk_ok(int32_t c) { return c == 64 || c == 128; }
 
 kda_status prefill_check(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *s0, const int32_t *cu,
@@ -76,7 +80,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     if (num_seqs == 0) return KDA_OK;
     const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
     const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, cu_seqlens,
-                                             num_seqs, seq_len, H, d_k, chunk_size,
+                                             num_seqs, seq_len, H, d_k, 64,
                                              dtype == KDA_BF16, o, final_state, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

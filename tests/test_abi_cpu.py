@@ -82,7 +82,7 @@ def _dec(**kw):
     (dict(num_seqs=3, total=128), ESHAPE),           # equal lengths need a multiple
     (dict(num_seqs=0, total=5), ESHAPE),
     (dict(dk=48, dv=48), EUNSUP), (dict(dk=64, dv=128), EUNSUP), (dict(dk=256, dv=256), EUNSUP),
-    (dict(chunk=32), EUNSUP), (dict(chunk=96), EUNSUP), (dict(dt=7), EUNSUP),
+    (dict(chunk=32), EUNSUP), (dict(chunk=96), EUNSUP), (dict(chunk=256), EUNSUP), (dict(dt=7), EUNSUP),
     (dict(dt=0, dk=128, dv=128), EUNSUP),            # fp32 path is for d <= 64
     (dict(q=MIS), EALIGN), (dict(g=MIS), EALIGN), (dict(o=MIS), EALIGN),
     (dict(s0=MIS), EALIGN), (dict(sf=MIS), EALIGN), (dict(cu=MIS), EALIGN),

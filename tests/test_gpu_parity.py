@@ -124,6 +124,23 @@ def test_prefill_k3_8k():
     assert eo <= 2e-2 and es <= 2e-2
 
 
+def test_prefill_chunk_128_equals_chunk_64_and_oracle():
+    w = inputs.custom(H=3, dk=128, dv=128, seqlens=[300, 129], state_std=0.05)
+    x = inputs.prefill_inputs(w, seed=17, device=DEV)
+    eo, es = run_prefill(x, 128)
+    report("prefill C=128 small", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+@pytest.mark.slow
+def test_prefill_k3_128k():
+    w = inputs.WORKLOADS["k3_prefill_128k"]
+    x = inputs.prefill_inputs(w, seed=3, device=DEV)
+    eo, es = run_prefill(x, w.chunk, heads=[0, 95])
+    report("prefill k3 128k (C=128)", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
 def test_prefill_varlen_prefix():
     w = inputs.WORKLOADS["k3_varlen_prefix"]
     x = inputs.prefill_inputs(w, seed=4, device=DEV)
