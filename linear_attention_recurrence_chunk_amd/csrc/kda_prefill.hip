@@ -138,9 +138,12 @@ __device__ __forceinline__ uint32_t row_off(int row, int64_t nvalid, int rowstri
 }
 
 // Loads are unconditional, so that no select on a loaded value makes the wave
-// wait for it.
+// wait for it.  `parts` selects what to load (LOAD_G, LOAD_KQ, LOAD_VB) so that
+// the next chunk's loads can be spread over the phases of the current one.
+enum { LOAD_G = 1, LOAD_KQ = 2, LOAD_VB = 4, LOAD_ALL = 7 };
+
 template <typename T, int DK, int BV>
-__device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, const SeqView &sv,
+__device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, const SeqView &sv,
                                            int64_t t0, const T *__restrict__ q,
                                            const T *__restrict__ k, const T *__restrict__ v,
                                            const float *__restrict__ g,
@@ -157,21 +160,25 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, const SeqVie
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t off = row_off(16 * I + 4 * qr + r, nvalid, rs) + 4 * c4;
-            R.g[r] = *reinterpret_cast<const f32x4 *>(g + cbase + off);
-            R.k[r] = *reinterpret_cast<const QV *>(k + cbase + off);
-            R.q[r] = *reinterpret_cast<const QV *>(q + cbase + off);
+            if (parts & LOAD_G) R.g[r] = *reinterpret_cast<const f32x4 *>(g + cbase + off);
+            if (parts & LOAD_KQ) {
+                R.k[r] = *reinterpret_cast<const QV *>(k + cbase + off);
+                R.q[r] = *reinterpret_cast<const QV *>(q + cbase + off);
+            }
         }
     }
-    const T *vb = v + (t0 * sv.H + sv.head) * DV + sv.v0;
+    if (parts & LOAD_VB) {
+        const T *vb = v + (t0 * sv.H + sv.head) * DV + sv.v0;
 #pragma unroll
-    for (int m = 0; m < Cf::NVV; ++m) {
-        const int vi = t + Cf::NT * m;
-        const int row = (vi / Cf::VPR) < Cf::C ? vi / Cf::VPR : Cf::C - 1, cv = vi % Cf::VPR;
-        R.v[m] = *reinterpret_cast<const f32x4 *>(vb + row_off(row, nvalid, sv.H * DV) +
-                                                  cv * (16 / (int)sizeof(T)));
+        for (int m = 0; m < Cf::NVV; ++m) {
+            const int vi = t + Cf::NT * m;
+            const int row = (vi / Cf::VPR) < Cf::C ? vi / Cf::VPR : Cf::C - 1, cv = vi % Cf::VPR;
+            R.v[m] = *reinterpret_cast<const f32x4 *>(vb + row_off(row, nvalid, sv.H * DV) +
+                                                      cv * (16 / (int)sizeof(T)));
+        }
+        const float *bb = beta + t0 * sv.H + sv.head;
+        R.beta = bb[row_off(t < Cf::C ? t : 0, nvalid, sv.H)];
     }
-    const float *bb = beta + t0 * sv.H + sv.head;
-    R.beta = bb[row_off(t < Cf::C ? t : 0, nvalid, sv.H)];
 }
 
 // Make this wave's LDS writes visible to its other lanes.
@@ -285,11 +292,12 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
 
     const int64_t nchunks = (sv.eos - sv.bos + C - 1) / C;
     ChunkRegs<T, DK, BV> R;
-    if (nchunks > 0) load_chunk(R, sv, sv.bos, q, k, v, g, beta, DV);
+    if (nchunks > 0) load_chunk(R, LOAD_ALL, sv, sv.bos, q, k, v, g, beta, DV);
 
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = sv.bos + ch * C;
         const int64_t nvalid = sv.eos - t0;              // rows of this chunk in the sequence
+        const bool full = nvalid >= C;
 
         // ================= E: sub-block-local decays and operand tiles
         {
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
                     float a[4], pl[4], sl[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        a[r] = (r0 + r < nvalid) ? __expf(R.g[r][cc]) : 1.f;
+                        a[r] = (full || r0 + r < nvalid) ? __expf(R.g[r][cc]) : 1.f;
                     pl[0] = a[0];
 #pragma unroll
                     for (int r = 1; r < 4; ++r) pl[r] = pl[r - 1] * a[r];
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
                     ebv[cc] = eb;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const bool in = r0 + r < nvalid;
+                        const bool in = full || r0 + r < nvalid;
                         const float kk = in ? to_f32(R.k[r][cc]) : 0.f;
                         const float qq = in ? to_f32(R.q[r][cc]) : 0.f;
                         const float eL = lead * pl[r];            // e^{L_r}
@@ -356,7 +364,8 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
                 *reinterpret_cast<f32x4 *>(&sm.V[row][cv * (16 / (int)sizeof(T))]) = R.v[m];
         }
         __syncthreads();   // ---------------------------------------------- B1
-        if (ch + 1 < nchunks) load_chunk(R, sv, t0 + C, q, k, v, g, beta, DV);
+        const bool more = ch + 1 < nchunks;
+        if (more) load_chunk(R, LOAD_G, sv, t0 + C, q, k, v, g, beta, DV);
 
         // ================= AP: 16x16 blocks (I, J <= I) of A and P, computed
         // transposed so that each lane ends with four consecutive columns of
@@ -421,6 +430,7 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
             }
         }
         __syncthreads();   // ---------------------------------------------- B2
+        if (more) load_chunk(R, LOAD_KQ, sv, t0 + C, q, k, v, g, beta, DV);
 
         f32x4 accZ[NVT];
         if (state_wave) {
@@ -500,6 +510,7 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
             }
         }
         __syncthreads();   // ---------------------------------------------- B3
+        if (more) load_chunk(R, LOAD_VB, sv, t0 + C, q, k, v, g, beta, DV);
 
         if (!state_wave) {
             // ============= forward substitution U_I = T_II (R_I - sum_{J<I} A_IJ U_J),
