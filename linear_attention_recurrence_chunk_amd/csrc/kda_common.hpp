@@ -19,6 +19,7 @@ namespace kda {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -57,12 +58,25 @@ template <> struct Path<bf16> {
         for (int e = 0; e < 8; ++e) x[e] = (float)f[e];
     }
     // K = 16 product: a holds A[n16][4*grp + i], b holds B[4*grp + i][n16], i = 0..3
-    __device__ __forceinline__ static f32x4 mma16(const float *a, const float *b, f32x4 c) {
-        bf16x4 av, bv;
+    typedef bf16x4 quad;
+    __device__ __forceinline__ static quad to_quad(const float *x) {
+        quad r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { av[i] = (bf16)a[i]; bv[i] = (bf16)b[i]; }
+        for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+        return r;
+    }
+    __device__ __forceinline__ static quad to_quad(f32x4 x) {
+        quad r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+        return r;
+    }
+    __device__ __forceinline__ static f32x4 mma16q(quad a, quad b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(short4v, av), __builtin_bit_cast(short4v, bv), c, 0, 0, 0);
+            __builtin_bit_cast(short4v, a), __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 mma16(const float *a, const float *b, f32x4 c) {
+        return mma16q(to_quad(a), to_quad(b), c);
     }
 };
 
@@ -75,10 +89,18 @@ template <> struct Path<float> {
     }
     __device__ __forceinline__ static frag pack(const float *x) { return x[0]; }
     __device__ __forceinline__ static void unpack(frag f, float *x) { x[0] = f; }
-    __device__ __forceinline__ static f32x4 mma16(const float *a, const float *b, f32x4 c) {
+    typedef f32x4 quad;
+    __device__ __forceinline__ static quad to_quad(const float *x) {
+        return f32x4{x[0], x[1], x[2], x[3]};
+    }
+    __device__ __forceinline__ static quad to_quad(f32x4 x) { return x; }
+    __device__ __forceinline__ static f32x4 mma16q(quad a, quad b, f32x4 c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
         return c;
+    }
+    __device__ __forceinline__ static f32x4 mma16(const float *a, const float *b, f32x4 c) {
+        return mma16q(to_quad(a), to_quad(b), c);
     }
 };
 

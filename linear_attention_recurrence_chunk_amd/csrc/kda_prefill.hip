@@ -18,93 +18,101 @@
 //
 // (I + A) is solved blockwise on 16-token sub-blocks: each diagonal block's
 // inverse comes from the identity (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8)
-// (N strictly lower 16 x 16, so N^16 = 0), evaluated with matrix-core products,
-// and U follows by block forward substitution
+// (N strictly lower 16 x 16, so N^16 = 0), evaluated on the matrix cores, and U
+// follows by block forward substitution
 //     U_I = (I + A_II)^-1 (R_I - sum_{J<I} A_IJ U_J),   R = B (V - (K o e^G) S).
 //
 // Decay factors never leave the float range.  With L the sub-block-local
 // inclusive cumulative sum of g and B_J the total log decay of sub-block J:
-//   rows of sub-block I:        e^{L_r}                          in [e^-80, 1]
-//   diagonal-block columns:     e^{-L_j}                         in [1, e^80]
-//   columns of J < I:           e^{B_J - L_j} * prod_{J<m<I} e^{B_m}   <= 1
+//   rows of sub-block I (row operand):   e^{L_r}                     in [e^-80, 1]
+//   columns (stored operand):            e^{-L_j}                    in [1, e^80]
+//   column operand of block (I, J < I):  e^{-L_j} prod_{J<=m<I} e^{B_m}   <= 1
 // e^80 is the bound the "Glossaire" entry "Decroissance bornee" gives for
 // g_min = -5 (16 tokens times 5; see also the box "Limite importante" of page
 // "Vecteurs, embeddings, espaces de representation").  A factor that
 // underflows is a product of true decays below 1e-38: no significant term is
 // lost.  Products are taken in an order in which no intermediate overflows.
 //
-// Work split (8 waves).  Waves 0-3 ("state waves") hold the fp32 state slice
-// in registers, invert the diagonal blocks and update the state; waves 4-7
-// ("row waves") own the 16-token row block I = wave - 4 for the state
-// read-out, the forward substitution (by value-column tile) and the output.
+// Work split: 16 waves, each with a fixed job in every phase of a chunk.
+//   E    all waves: decays of a (16-token sub-block, channel pair, 4 rows) item
+//        and the operand tiles K o e^L, Q o e^L, K o e^-L (and its transpose).
+//   AP   waves 0-3: diagonal block I of A and P and the inverse of I + A_II,
+//        kept in registers; waves 4-15: one off-diagonal block of A or of P.
+//   YZ   wave (I, value tile): (K o e^G) S and (Q o e^G) S for its 16 rows and
+//        16 value columns, then R = B (V - (K o e^G) S).
+//   U    one wave per 16 value columns: the forward substitution.
+//   SO   every wave: its state tiles S' = Diag(gamma) S + Kbar^T U, and its
+//        (I, value tile) block of O = (Q o e^G) S + P U, stored to o.
 // Contractions run on the matrix cores (v_mfma_f32_16x16x32_bf16 and
 // v_mfma_f32_16x16x16_bf16, or v_mfma_f32_16x16x4_f32 for fp32 inputs) with
-// fp32 accumulation; operands are rounded to the input type.  The next chunk's
-// raw inputs are loaded into registers one chunk ahead.
+// fp32 accumulation; operands are rounded to the input type.  The fp32 state
+// stays in registers across the chunk loop.  The next chunk's raw inputs are
+// loaded into registers one chunk ahead.
 #include "kda_common.hpp"
 
 namespace kda {
 
 template <typename T, int DK, int BV>
-struct Cfg64 {
+struct Cfg {
     static constexpr int C = 64;
     static constexpr int NB = 4;                      // 16-token sub-blocks
-    static constexpr int NW = 8;
+    static constexpr int NW = 16;
     static constexpr int NT = 64 * NW;
     static constexpr int PAD = 16 / (int)sizeof(T);   // 16-byte row padding
     static constexpr int LDK = DK + PAD;              // [token][channel] tiles
     static constexpr int LDC = C + PAD;               // [.][token] tiles
+    static constexpr int LDV = BV + PAD;              // value slice rows
     static constexpr int LD16 = 16 + PAD;             // 16 x 16 tiles
-    // elementwise items: (sub-block, 4 channels, 4 rows); the four row
-    // quarters of one channel quad sit in the four 16-lane groups of a wave
-    static constexpr int QPW = (DK / 4 < 16) ? DK / 4 : 16;   // quads per lane group
-    static constexpr int WPB = (DK / 64 > 1) ? DK / 64 : 1;   // waves per sub-block
-    static constexpr int EWAVES = NB * WPB;                   // waves doing elementwise
-    static constexpr int VPR = BV * (int)sizeof(T) / 16;      // 16-byte vectors per V row
-    static constexpr int NVV = (C * VPR + NT - 1) / NT;
+    static constexpr int WPB = DK / 32;               // E waves per sub-block
+    static constexpr int EWAVES = NB * WPB;
     static constexpr int NCT = DK / 16;               // state row tiles
     static constexpr int NVT = BV / 16;               // state column tiles
-    static constexpr int SWPC = (NCT >= 4) ? 1 : 4 / NCT;   // state waves per row tile
-    static constexpr int SCT = (NCT >= 4) ? NCT / 4 : 1;    // row tiles per state wave
-    static constexpr int SVT = NVT / SWPC;                   // column tiles per state wave
+    static constexpr int NTILE = NCT * NVT;
+    static constexpr int NST = (NTILE + NW - 1) / NW; // state tiles per wave
+    static constexpr int NJOB = NB * NVT;             // (row block, value tile) jobs
+    static constexpr int VEC = 8 / (int)sizeof(T);    // elements per 8-byte vector
+    static constexpr int VPR = BV / VEC;              // 8-byte vectors per value row
+    static constexpr int NVV = (C * VPR + NT - 1) / NT;
+    static_assert(DK % 32 == 0 && DK <= 128, "head size");
+    static_assert(BV % 16 == 0 && NJOB <= NW, "value slice");
     static_assert(EWAVES <= NW, "elementwise mapping");
-    static_assert(SVT >= 1 && NVT % SWPC == 0, "state tiling");
+    static_assert(NTILE <= NW || (NTILE % NW == 0 && NW % NCT == 0), "state tiling");
     static_assert(DK % Path<T>::KS == 0 && C % Path<T>::KS == 0, "k steps");
 };
 
 template <typename T, int DK, int BV>
-struct Smem64 {
-    typedef Cfg64<T, DK, BV> Cf;
-    T Kr[Cf::C][Cf::LDK];      // K o e^{L}        row operand
-    T Qr[Cf::C][Cf::LDK];      // Q o e^{L}
-    T Kc[Cf::C][Cf::LDK];      // K o e^{B - L}    column operand of blocks J < I
-    T Kd[Cf::C][Cf::LDK];      // K o e^{-L}       column operand of diagonal blocks
-    T P[Cf::C][Cf::LDC];       // Tril((Q o e^G)(K o e^-G)^T)
-    T A[Cf::C][Cf::LDC];       // A (beta applied, strictly lower)
-    T ST[BV][Cf::LDK];         // state slice, transposed operand copy
-    T RT[BV][Cf::LDC];         // R^T, overwritten in place by U^T
-    T V[Cf::C][BV];            // value slice
-    T Tm[Cf::NB][16][Cf::LD16];      // diagonal blocks of (I + A)^-1
-    T scr[4][2][16][Cf::LD16];       // per-wave N^2, N^4 for the diagonal inverses
-    float eB[Cf::NB][DK];      // e^{B_J}
-    float eE[Cf::NB + 1][DK];  // e^{E_J} = prod_{m<J} e^{B_m}; row NB: whole-chunk decay
-    float eT[Cf::NB][DK];      // prod_{m>J} e^{B_m}
+struct Smem {
+    typedef Cfg<T, DK, BV> Cf;
+    T Kr[Cf::C][Cf::LDK];       // K o e^{L}         row operand
+    T Qr[Cf::C][Cf::LDK];       // Q o e^{L}
+    T Kd[Cf::C][Cf::LDK];       // K o e^{-L}        column operand
+    T KdT[DK][Cf::LDC];         // the same, [channel][token]
+    T P[Cf::C][Cf::LDC];        // Tril((Q o e^G)(K o e^-G)^T)
+    T An[Cf::C][Cf::LDC];       // -A, blocks J < I
+    T Tm[Cf::NB][16][Cf::LD16]; // (I + A_II)^-1
+    T ST[BV][Cf::LDK];          // state slice, transposed operand copy
+    T RT[BV][Cf::LDC];          // R^T, overwritten in place by U^T
+    T V[Cf::C][Cf::LDV];        // value slice
+    float eB[Cf::NB][DK];       // e^{B_J}
+    float eE[Cf::NB + 1][DK];   // prod_{m<J} e^{B_m}; row NB: whole-chunk decay
+    float eTi[Cf::NB][DK];      // prod_{m>=J} e^{B_m}
     float beta[Cf::C];
 };
 
-template <typename T> struct Quad;
-template <> struct Quad<bf16> { typedef bf16x4 type; };
-template <> struct Quad<float> { typedef f32x4 type; };
+// two and four elements; `eight_bytes` is the 8-byte vector of the value loads
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { typedef bf16x2 two; typedef bf16x4 four; typedef bf16x4 eight_bytes; };
+template <> struct Vec<float> { typedef f32x2 two; typedef f32x4 four; typedef f32x2 eight_bytes; };
 
 // Raw inputs of one chunk, held in registers one chunk ahead: for the
-// elementwise item of this thread, four rows of four channels of g, k, q;
+// elementwise item of this thread, four rows of two channels of g, k, q;
 // plus a share of the value slice and one beta.
 template <typename T, int DK, int BV>
 struct ChunkRegs {
-    typedef Cfg64<T, DK, BV> Cf;
-    f32x4 g[4];
-    typename Quad<T>::type k[4], q[4];
-    f32x4 v[Cf::NVV];
+    typedef Cfg<T, DK, BV> Cf;
+    f32x2 g[4];
+    typename Vec<T>::two k[4], q[4];
+    typename Vec<T>::eight_bytes v[Cf::NVV];
     float beta;
 };
 
@@ -113,19 +121,6 @@ struct SeqView {
     int head, H;
     int v0;             // first value column of the slice
 };
-
-// Elementwise item of thread t: sub-block I, channel quad c4 (channels
-// 4 c4 .. 4 c4 + 3), row quarter qr (rows 4 qr .. 4 qr + 3 of the sub-block).
-template <int DK, int QPW, int WPB>
-__device__ __forceinline__ bool item_of(int t, int &I, int &c4, int &qr)
-{
-    const int w = t >> 6, l = t & 63;
-    qr = l >> 4;
-    const int qi = l & 15;
-    I = w / WPB;
-    c4 = (w % WPB) * QPW + qi;
-    return qi < QPW && w < 4 * WPB;
-}
 
 // Offset (in elements) of row `row` of the chunk, clamped to the last row of
 // the sequence: rows past the end read a valid address and are zeroed where
@@ -149,21 +144,22 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
                                            const float *__restrict__ g,
                                            const float *__restrict__ beta, int DV)
 {
-    typedef Cfg64<T, DK, BV> Cf;
-    typedef typename Quad<T>::type QV;
-    const int t = threadIdx.x;
+    typedef Cfg<T, DK, BV> Cf;
+    typedef typename Vec<T>::two V2;
+    typedef typename Vec<T>::eight_bytes V8;
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
     const int64_t nvalid = sv.eos - t0;
     const int64_t cbase = (t0 * sv.H + sv.head) * DK;      // wave-uniform
     const int rs = sv.H * DK;                              // row stride, elements
-    int I, c4, qr;
-    if (item_of<DK, Cf::QPW, Cf::WPB>(t, I, c4, qr)) {
+    if (wv < Cf::EWAVES) {
+        const int I = wv / Cf::WPB, cp = (wv % Cf::WPB) * 16 + (lane & 15), qr = lane >> 4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const uint32_t off = row_off(16 * I + 4 * qr + r, nvalid, rs) + 4 * c4;
-            if (parts & LOAD_G) R.g[r] = *reinterpret_cast<const f32x4 *>(g + cbase + off);
+            const uint32_t off = row_off(16 * I + 4 * qr + r, nvalid, rs) + 2 * cp;
+            if (parts & LOAD_G) R.g[r] = *reinterpret_cast<const f32x2 *>(g + cbase + off);
             if (parts & LOAD_KQ) {
-                R.k[r] = *reinterpret_cast<const QV *>(k + cbase + off);
-                R.q[r] = *reinterpret_cast<const QV *>(q + cbase + off);
+                R.k[r] = *reinterpret_cast<const V2 *>(k + cbase + off);
+                R.q[r] = *reinterpret_cast<const V2 *>(q + cbase + off);
             }
         }
     }
@@ -173,20 +169,23 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
         for (int m = 0; m < Cf::NVV; ++m) {
             const int vi = t + Cf::NT * m;
             const int row = (vi / Cf::VPR) < Cf::C ? vi / Cf::VPR : Cf::C - 1, cv = vi % Cf::VPR;
-            R.v[m] = *reinterpret_cast<const f32x4 *>(vb + row_off(row, nvalid, sv.H * DV) +
-                                                      cv * (16 / (int)sizeof(T)));
+            R.v[m] = *reinterpret_cast<const V8 *>(vb + row_off(row, nvalid, sv.H * DV) +
+                                                   cv * Cf::VEC);
         }
         const float *bb = beta + t0 * sv.H + sv.head;
         R.beta = bb[row_off(t < Cf::C ? t : 0, nvalid, sv.H)];
     }
 }
 
-// Make this wave's LDS writes visible to its other lanes.
-__device__ __forceinline__ void wave_lds_sync()
+// The lane index, hidden from the optimiser.  Taken at the start of each phase
+// of the chunk loop, it keeps per-lane LDS addresses from being hoisted out of
+// the loop: they are cheap to recompute, while keeping them all live would
+// spill registers to scratch memory.
+__device__ __forceinline__ int opaque_lane()
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int l = __lane_id();
+    asm volatile("" : "+v"(l));
+    return l;
 }
 
 template <int N> __device__ __forceinline__ void load_f32(float *dst, const float *src)
@@ -203,29 +202,119 @@ template <int N> __device__ __forceinline__ void load_f32(float *dst, const floa
     }
 }
 
-// Four consecutive elements, packed for one store.
-template <typename T> __device__ __forceinline__ typename Quad<T>::type pack4(const float *x)
+template <typename T> __device__ __forceinline__ typename Vec<T>::two pack2(float a, float b)
 {
-    typename Quad<T>::type r;
+    typename Vec<T>::two r;
+    r[0] = from_f32<T>(a);
+    r[1] = from_f32<T>(b);
+    return r;
+}
+
+template <typename T> __device__ __forceinline__ typename Vec<T>::four pack4(const float *x)
+{
+    typename Vec<T>::four r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = from_f32<T>(x[i]);
     return r;
 }
 
+template <typename T> __device__ __forceinline__ void unpack4(typename Vec<T>::four v, float *x)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = to_f32(v[i]);
+}
+
+
+// Off-diagonal block (I, J < I) of A (IS_P false; stored negated, beta
+// applied) or of P.  The column operand K o e^{-L_j} is brought to the
+// reference of row block I by prod_{J<=m<I} e^{B_m}.  The product is taken
+// transposed so that each lane ends with four consecutive columns of one row.
+template <int I, int J, bool IS_P, typename T, int DK, int BV>
+__device__ __forceinline__ void ap_offdiag(Smem<T, DK, BV> &sm, int n16, int grp)
+{
+    typedef Path<T> PT;
+    typedef typename Vec<T>::four V4;
+    constexpr int KS = PT::KS, KPL = PT::KPL;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DK / KS; ++ks) {
+        const int kc = ks * KS + grp * KPL;
+        float x[KPL], f[KPL];
+        PT::unpack(load_frag<T>(&sm.Kd[16 * J + n16][kc]), x);
+        load_f32<KPL>(f, &sm.eB[J][kc]);
+#pragma unroll
+        for (int m = J + 1; m < I; ++m) {
+            float f2[KPL];
+            load_f32<KPL>(f2, &sm.eB[m][kc]);
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) f[e] *= f2[e];
+        }
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) x[e] *= f[e];
+        const typename PT::frag col = PT::pack(x);
+        const typename PT::frag row =
+            load_frag<T>(IS_P ? &sm.Qr[16 * I + n16][kc] : &sm.Kr[16 * I + n16][kc]);
+        acc = PT::mma(col, row, acc);
+    }
+    // lane holds X[r][j], r = 16 I + n16, j = 16 J + 4 grp + i
+    const int r = 16 * I + n16;
+    float w[4];
+    if (IS_P) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = acc[i];
+        *reinterpret_cast<V4 *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(w);
+    } else {
+        const float nb = -sm.beta[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = nb * acc[i];
+        *reinterpret_cast<V4 *>(&sm.An[r][16 * J + 4 * grp]) = pack4<T>(w);
+    }
+}
+
+// (K o e^G) S and (Q o e^G) S for row block I and value tile vt.  The decay
+// e^{E_I} from the chunk start to sub-block I scales the state operand (one
+// fragment serves both products).  Y comes back in the D layout (rows of the
+// block in 4 grp + i, value columns in n16); Z transposed (value columns in
+// 4 grp + i, rows in n16), as the output's transposed product needs it.
+template <bool SCALE, typename T, int DK, int BV>
+__device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt, int n16, int grp,
+                                         f32x4 &Y, f32x4 &Zt)
+{
+    typedef Path<T> PT;
+    constexpr int KS = PT::KS, KPL = PT::KPL;
+#pragma unroll
+    for (int ks = 0; ks < DK / KS; ++ks) {
+        const int kc = ks * KS + grp * KPL;
+        typename PT::frag s = load_frag<T>(&sm.ST[16 * vt + n16][kc]);
+        if (SCALE) {
+            float x[KPL], f[KPL];
+            PT::unpack(s, x);
+            load_f32<KPL>(f, &sm.eE[I][kc]);
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) x[e] *= f[e];
+            s = PT::pack(x);
+        }
+        Y = PT::mma(load_frag<T>(&sm.Kr[16 * I + n16][kc]), s, Y);
+        Zt = PT::mma(s, load_frag<T>(&sm.Qr[16 * I + n16][kc]), Zt);
+    }
+}
+
 template <typename T, int DK, int BV, int DV>
-__global__ __launch_bounds__(512, 1) void prefill64_kernel(
+__global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ s0, const int32_t *__restrict__ cu_seqlens, int num_seqs,
     int64_t seq_len, int H, T *__restrict__ o, float *__restrict__ sfinal)
 {
-    typedef Cfg64<T, DK, BV> Cf;
+    typedef Cfg<T, DK, BV> Cf;
     typedef Path<T> PT;
-    typedef Smem64<T, DK, BV> Sm;
-    typedef typename Quad<T>::type QV;
+    typedef Smem<T, DK, BV> Sm;
+    typedef typename Vec<T>::two V2;
+    typedef typename Vec<T>::four V4;
+    typedef typename Vec<T>::eight_bytes V8;
     constexpr int C = Cf::C, NB = Cf::NB, NT = Cf::NT, KS = PT::KS, KPL = PT::KPL;
     constexpr int NSLICE = DV / BV;
-    constexpr int NVT = Cf::NVT;
+    constexpr int NVT = Cf::NVT, NCT = Cf::NCT, NST = Cf::NST;
     __shared__ __align__(16) Sm sm;
 
     // ---- work item: (sequence, head, value slice); slices of one head adjacent
@@ -252,43 +341,35 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
     const int t = threadIdx.x;
     const int lane = lane_id(), wv = wave_id();
     const int n16 = lane & 15, grp = lane >> 4;
-    const bool state_wave = wv < 4;
-    const int I_row = wv - 4;                        // row block of a row wave
 
-    // ---- state slice in the registers of the state waves, D layout:
-    // tile (ct, vt) holds S[16 ct + 4 grp + i][16 vt + n16]
-    const int sw = state_wave ? wv : 0;
-    const int ct0 = (sw / Cf::SWPC) * Cf::SCT;
-    const int vt0 = (sw % Cf::SWPC) * Cf::SVT;
-    f32x4 S[Cf::SCT][Cf::SVT];
+    // ---- state tiles of this wave, D layout: tile (ct, vt) holds
+    // S[16 ct + 4 grp + i][16 vt + n16].  Tiles wv, wv + 16, ... share one ct.
+    const int ct = wv % NCT;
+    f32x4 S[NST];
     const int64_t sbase = ((int64_t)seq * H + head) * (int64_t)(DK * DV) + sv.v0;
 #pragma unroll
-    for (int a = 0; a < Cf::SCT; ++a)
-#pragma unroll
-        for (int bq = 0; bq < Cf::SVT; ++bq) {
-            S[a][bq] = zero4();
-            if (state_wave && s0) {
+    for (int s = 0; s < NST; ++s) {
+        S[s] = zero4();
+        const int tl = wv + Cf::NW * s, vt = tl / NCT;
+        if (tl < Cf::NTILE) {
+            if (s0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[a][bq][i] = s0[sbase + (int64_t)(16 * (ct0 + a) + 4 * grp + i) * DV +
-                                     16 * (vt0 + bq) + n16];
+                    S[s][i] = s0[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16];
             }
+            float s4[4] = {S[s][0], S[s][1], S[s][2], S[s][3]};
+            *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
         }
-    if (state_wave) {
-#pragma unroll
-        for (int a = 0; a < Cf::SCT; ++a)
-#pragma unroll
-            for (int bq = 0; bq < Cf::SVT; ++bq)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sm.ST[16 * (vt0 + bq) + n16][16 * (ct0 + a) + 4 * grp + i] =
-                        from_f32<T>(S[a][bq][i]);
     }
     // constant zero blocks above the diagonal of P
     for (int e = t; e < C * C; e += NT) {
         const int r = e / C, j = e % C;
         if ((j >> 4) > (r >> 4)) sm.P[r][j] = from_f32<T>(0.f);
     }
+
+    // (row block, value tile) job of this wave in the YZ and output phases
+    const bool has_job = wv < Cf::NJOB;
+    const int jI = wv / NVT, jvt = wv % NVT;
 
     const int64_t nchunks = (sv.eos - sv.bos + C - 1) / C;
     ChunkRegs<T, DK, BV> R;
@@ -300,323 +381,271 @@ __global__ __launch_bounds__(512, 1) void prefill64_kernel(
         const bool full = nvalid >= C;
 
         // ================= E: sub-block-local decays and operand tiles
-        {
-            int I, c4, qr;
-            if (item_of<DK, Cf::QPW, Cf::WPB>(t, I, c4, qr)) {
-                const int r0 = 16 * I + 4 * qr;
-                float kr[4][4], qrw[4][4], kc[4][4], kd[4][4], ebv[4];
+        if (wv < Cf::EWAVES) {
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const int I = wv / Cf::WPB, cp = (wv % Cf::WPB) * 16 + n16, qr = grp;
+            const int r0 = 16 * I + 4 * qr;
+            float kr[4][2], qv[4][2], kd[4][2], ebv[2];
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    float a[4], pl[4], sl[4];
+            for (int cc = 0; cc < 2; ++cc) {
+                float a[4], pl[4], sl[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        a[r] = (full || r0 + r < nvalid) ? __expf(R.g[r][cc]) : 1.f;
-                    pl[0] = a[0];
+                for (int r = 0; r < 4; ++r)
+                    a[r] = (full || r0 + r < nvalid) ? __expf(R.g[r][cc]) : 1.f;
+                pl[0] = a[0];
 #pragma unroll
-                    for (int r = 1; r < 4; ++r) pl[r] = pl[r - 1] * a[r];
-                    sl[3] = 1.f;
+                for (int r = 1; r < 4; ++r) pl[r] = pl[r - 1] * a[r];
+                sl[3] = 1.f;
 #pragma unroll
-                    for (int r = 2; r >= 0; --r) sl[r] = sl[r + 1] * a[r + 1];
-                    // decays of the four row quarters of this sub-block
-                    float qd[4];
+                for (int r = 2; r >= 0; --r) sl[r] = sl[r + 1] * a[r + 1];
+                // decays of the four row quarters of this sub-block
+                float qd[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) qd[j] = __shfl(pl[3], (lane & 15) + 16 * j);
-                    float lead = 1.f, tail = 1.f;
+                for (int j = 0; j < 4; ++j) qd[j] = __shfl(pl[3], n16 + 16 * j);
+                float lead = 1.f, tail = 1.f;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (j < qr) lead *= qd[j];
-                        if (j > qr) tail *= qd[j];
-                    }
-                    const float eb = ((qd[0] * qd[1]) * qd[2]) * qd[3];
-                    const float rb = __builtin_amdgcn_rcpf(eb);     // <= e^80
-                    ebv[cc] = eb;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const bool in = full || r0 + r < nvalid;
-                        const float kk = in ? to_f32(R.k[r][cc]) : 0.f;
-                        const float qq = in ? to_f32(R.q[r][cc]) : 0.f;
-                        const float eL = lead * pl[r];            // e^{L_r}
-                        const float sfx = sl[r] * tail;           // e^{B - L_r}
-                        kr[r][cc] = kk * eL;
-                        qrw[r][cc] = qq * eL;
-                        kc[r][cc] = kk * sfx;
-                        kd[r][cc] = (kk * sfx) * rb;              // e^{-L_r}, <= e^80
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    if (j < qr) lead *= qd[j];
+                    if (j > qr) tail *= qd[j];
                 }
+                const float eb = ((qd[0] * qd[1]) * qd[2]) * qd[3];
+                const float rb = __builtin_amdgcn_rcpf(eb);     // <= e^80
+                ebv[cc] = eb;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    *reinterpret_cast<QV *>(&sm.Kr[r0 + r][4 * c4]) = pack4<T>(kr[r]);
-                    *reinterpret_cast<QV *>(&sm.Qr[r0 + r][4 * c4]) = pack4<T>(qrw[r]);
-                    *reinterpret_cast<QV *>(&sm.Kc[r0 + r][4 * c4]) = pack4<T>(kc[r]);
-                    *reinterpret_cast<QV *>(&sm.Kd[r0 + r][4 * c4]) = pack4<T>(kd[r]);
+                    const bool in = full || r0 + r < nvalid;
+                    const float kk = in ? to_f32(R.k[r][cc]) : 0.f;
+                    const float qq = in ? to_f32(R.q[r][cc]) : 0.f;
+                    const float eL = lead * pl[r];            // e^{L_r}
+                    const float sfx = sl[r] * tail;           // e^{B - L_r}
+                    kr[r][cc] = kk * eL;
+                    qv[r][cc] = qq * eL;
+                    kd[r][cc] = (kk * sfx) * rb;              // e^{-L_r}, <= e^80
                 }
-                if (qr == 0)
-                    *reinterpret_cast<f32x4 *>(&sm.eB[I][4 * c4]) =
-                        f32x4{ebv[0], ebv[1], ebv[2], ebv[3]};
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                *reinterpret_cast<V2 *>(&sm.Kr[r0 + r][2 * cp]) = pack2<T>(kr[r][0], kr[r][1]);
+                *reinterpret_cast<V2 *>(&sm.Qr[r0 + r][2 * cp]) = pack2<T>(qv[r][0], qv[r][1]);
+                *reinterpret_cast<V2 *>(&sm.Kd[r0 + r][2 * cp]) = pack2<T>(kd[r][0], kd[r][1]);
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                float c4[4] = {kd[0][cc], kd[1][cc], kd[2][cc], kd[3][cc]};
+                *reinterpret_cast<V4 *>(&sm.KdT[2 * cp + cc][r0]) = pack4<T>(c4);
+            }
+            if (qr == 0) *reinterpret_cast<f32x2 *>(&sm.eB[I][2 * cp]) = f32x2{ebv[0], ebv[1]};
         }
         if (t < C) sm.beta[t] = t < nvalid ? R.beta : 0.f;     // beta = 0 masks rows past the end
 #pragma unroll
         for (int m = 0; m < Cf::NVV; ++m) {
             const int vi = t + NT * m;
             const int row = vi / Cf::VPR, cv = vi % Cf::VPR;
-            if (row < C)
-                *reinterpret_cast<f32x4 *>(&sm.V[row][cv * (16 / (int)sizeof(T))]) = R.v[m];
+            if (row < C) *reinterpret_cast<V8 *>(&sm.V[row][cv * Cf::VEC]) = R.v[m];
         }
         __syncthreads();   // ---------------------------------------------- B1
         const bool more = ch + 1 < nchunks;
         if (more) load_chunk(R, LOAD_G, sv, t0 + C, q, k, v, g, beta, DV);
 
-        // ================= AP: 16x16 blocks (I, J <= I) of A and P, computed
-        // transposed so that each lane ends with four consecutive columns of
-        // one row
-        for (int p = wv; p < NB * (NB + 1) / 2; p += Cf::NW) {
-            int I = 0, rem = p;
-            while (rem > I) { rem -= I + 1; ++I; }
-            const int J = rem;
-            f32x4 accA = zero4(), accP = zero4();
+        // ================= AP
+        if (wv < NB) {
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            // diagonal block I: A_II both ways round, P_II, then (I + A_II)^-1
+            const int I = wv;
+            f32x4 accAt = zero4(), accA = zero4(), accPt = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / KS; ++ks) {
                 const int kc = ks * KS + grp * KPL;
-                typename PT::frag ac;
-                if (I == J) {
-                    ac = load_frag<T>(&sm.Kd[16 * J + n16][kc]);
-                } else if (I == J + 1) {
-                    ac = load_frag<T>(&sm.Kc[16 * J + n16][kc]);
-                } else {                                       // times prod_{J<m<I} e^{B_m}
-                    float x[KPL], f[KPL];
-                    PT::unpack(load_frag<T>(&sm.Kc[16 * J + n16][kc]), x);
-                    load_f32<KPL>(f, &sm.eB[J + 1][kc]);
-                    if (I == J + 3) {
-                        float f2[KPL];
-                        load_f32<KPL>(f2, &sm.eB[J + 2][kc]);
-#pragma unroll
-                        for (int e = 0; e < KPL; ++e) f[e] *= f2[e];
-                    }
-#pragma unroll
-                    for (int e = 0; e < KPL; ++e) x[e] *= f[e];
-                    ac = PT::pack(x);
-                }
-                accA = PT::mma(ac, load_frag<T>(&sm.Kr[16 * I + n16][kc]), accA);
-                accP = PT::mma(ac, load_frag<T>(&sm.Qr[16 * I + n16][kc]), accP);
+                const typename PT::frag fd = load_frag<T>(&sm.Kd[16 * I + n16][kc]);
+                const typename PT::frag fk = load_frag<T>(&sm.Kr[16 * I + n16][kc]);
+                const typename PT::frag fq = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
+                accAt = PT::mma(fd, fk, accAt);   // [r = n16][j = 4 grp + i]
+                accA = PT::mma(fk, fd, accA);     // [r = 4 grp + i][j = n16]
+                accPt = PT::mma(fd, fq, accPt);   // [r = n16][j = 4 grp + i]
             }
-            // lane holds A[r][j], P[r][j] for r = 16 I + n16, j = 16 J + 4 grp + i
-            const int r = 16 * I + n16;
-            const float br = sm.beta[r];
-            float va[4], vp[4];
+            // N = A_II in the A-operand layout (Na: N[n16][4 grp + i]) and in the
+            // D layout (Nd: N[4 grp + i][n16])
+            const float br = sm.beta[16 * I + n16];
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * I + 4 * grp]);
+            float Na[4], Nd[4], pv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int jl = 4 * grp + i;
-                va[i] = (I != J || jl < n16) ? accA[i] * br : 0.f;
-                vp[i] = (I != J || jl <= n16) ? accP[i] : 0.f;
+                Na[i] = jl < n16 ? br * accAt[i] : 0.f;
+                Nd[i] = n16 < jl ? b4[i] * accA[i] : 0.f;
+                pv[i] = jl <= n16 ? accPt[i] : 0.f;
             }
-            *reinterpret_cast<QV *>(&sm.A[r][16 * J + 4 * grp]) = pack4<T>(va);
-            *reinterpret_cast<QV *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(vp);
-        }
-        // decay tables: e^{E_J}, whole-chunk decay, decay after J
-        for (int e = t; e < (2 * NB + 1) * DK; e += NT) {
-            const int J = e / DK, c = e % DK;
-            float f = 1.f;
-            if (J <= NB) {
+            *reinterpret_cast<V4 *>(&sm.P[16 * I + n16][16 * I + 4 * grp]) = pack4<T>(pv);
+            // A lane's values of X in the A layout are those of X^T in the D
+            // layout.  So mma16(Xd, Xa), which multiplies X^T by X^T, returns
+            // (X^2)^T in the D layout, i.e. X^2 in the A layout: every power of
+            // N comes in both layouts without a transpose through LDS.
+            typedef typename PT::quad Q4;
+            const Q4 na = PT::to_quad(Na), nd = PT::to_quad(Nd);
+            const Q4 n2d = PT::to_quad(PT::mma16q(na, nd, zero4()));
+            const Q4 n2a = PT::to_quad(PT::mma16q(nd, na, zero4()));
+            const Q4 n4d = PT::to_quad(PT::mma16q(n2a, n2d, zero4()));
+            const Q4 n4a = PT::to_quad(PT::mma16q(n2d, n2a, zero4()));
+            // T^T = (I - N^T)(I + (N^2)^T)(I + (N^4)^T)(I + (N^8)^T) (the factors
+            // commute), built in the D layout, which holds T in the A layout:
+            // the lane ends with T[n16][4 grp + i]
+            f32x4 X = PT::mma16q(n4d, n4a, zero4());              // (N^8)^T
 #pragma unroll
-                for (int m = 0; m < NB; ++m)
-                    if (m < J) f *= sm.eB[m][c];
-                sm.eE[J][c] = f;
-            } else {
+            for (int i = 0; i < 4; ++i) X[i] += (4 * grp + i == n16) ? 1.f : 0.f;
+            X = PT::mma16q(n4d, PT::to_quad(X), X);                // (I + (N^4)^T)(...)
+            X = PT::mma16q(n2d, PT::to_quad(X), X);                // (I + (N^2)^T)(...)
+            float mNd[4];
 #pragma unroll
-                for (int m = 0; m < NB; ++m)
-                    if (m > J - NB - 1) f *= sm.eB[m][c];
-                sm.eT[J - NB - 1][c] = f;
+            for (int i = 0; i < 4; ++i) mNd[i] = -Nd[i];
+            X = PT::mma16q(PT::to_quad(mNd), PT::to_quad(X), X);  // (I - N^T)(...)
+            *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(X);
+        } else if (wv < NB + 12) {
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            switch (wv - NB) {
+                case 0: ap_offdiag<1, 0, false>(sm, n16, grp); break;
+                case 1: ap_offdiag<1, 0, true>(sm, n16, grp); break;
+                case 2: ap_offdiag<2, 1, false>(sm, n16, grp); break;
+                case 3: ap_offdiag<2, 1, true>(sm, n16, grp); break;
+                case 4: ap_offdiag<3, 2, false>(sm, n16, grp); break;
+                case 5: ap_offdiag<3, 2, true>(sm, n16, grp); break;
+                case 6: ap_offdiag<2, 0, false>(sm, n16, grp); break;
+                case 7: ap_offdiag<2, 0, true>(sm, n16, grp); break;
+                case 8: ap_offdiag<3, 1, false>(sm, n16, grp); break;
+                case 9: ap_offdiag<3, 1, true>(sm, n16, grp); break;
+                case 10: ap_offdiag<3, 0, false>(sm, n16, grp); break;
+                default: ap_offdiag<3, 0, true>(sm, n16, grp); break;
+            }
+            // decay tables, one channel per thread
+            const int c = t - 64 * NB;
+            if (c < DK) {
+                float e[NB];
+#pragma unroll
+                for (int m = 0; m < NB; ++m) e[m] = sm.eB[m][c];
+                float f = 1.f;
+#pragma unroll
+                for (int m = 0; m <= NB; ++m) {
+                    sm.eE[m][c] = f;
+                    if (m < NB) f *= e[m];
+                }
+                f = 1.f;
+#pragma unroll
+                for (int m = NB - 1; m >= 0; --m) {
+                    f *= e[m];
+                    sm.eTi[m][c] = f;
+                }
             }
         }
         __syncthreads();   // ---------------------------------------------- B2
         if (more) load_chunk(R, LOAD_KQ, sv, t0 + C, q, k, v, g, beta, DV);
 
-        f32x4 accZ[NVT];
-        if (state_wave) {
-            // ============= diagonal-block inverses (I + N)^-1, N = A_II
-            const int I = wv;
-            float dN[4], aN[4], aN2[4], aN4[4];
+        // ================= YZ: state read-out and R = B (V - Y), stored transposed
+        f32x4 Zt = zero4();
+        if (has_job) {
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            f32x4 Y = zero4();
+            if (jI == 0) yz_block<false>(sm, 0, jvt, n16, grp, Y, Zt);
+            else yz_block<true>(sm, jI, jvt, n16, grp, Y, Zt);
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * jI + 4 * grp]);
+            float rv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dN[i] = to_f32(sm.A[16 * I + 4 * grp + i][16 * I + n16]);
-                aN[i] = to_f32(sm.A[16 * I + n16][16 * I + 4 * grp + i]);
-            }
-            const f32x4 N2 = PT::mma16(aN, dN, zero4());
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.scr[I][0][4 * grp + i][n16] = from_f32<T>(N2[i]);
-            wave_lds_sync();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) aN2[i] = to_f32(sm.scr[I][0][n16][4 * grp + i]);
-            float bN2[4] = {N2[0], N2[1], N2[2], N2[3]};
-            const f32x4 N4 = PT::mma16(aN2, bN2, zero4());
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.scr[I][1][4 * grp + i][n16] = from_f32<T>(N4[i]);
-            wave_lds_sync();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) aN4[i] = to_f32(sm.scr[I][1][n16][4 * grp + i]);
-            float bN4[4] = {N4[0], N4[1], N4[2], N4[3]};
-            f32x4 X = PT::mma16(aN4, bN4, zero4());            // N^8
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[i] += (4 * grp + i == n16) ? 1.f : 0.f;   // I + N^8
-            float bX[4] = {X[0], X[1], X[2], X[3]};
-            X = PT::mma16(aN4, bX, X);                           // (I + N^4)(I + N^8)
-            float bY[4] = {X[0], X[1], X[2], X[3]};
-            X = PT::mma16(aN2, bY, X);                           // (I + N^2)(...)
-            float bZ[4] = {X[0], X[1], X[2], X[3]}, maN[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) maN[i] = -aN[i];
-            X = PT::mma16(maN, bZ, X);                           // (I - N)(...)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.Tm[I][4 * grp + i][n16] = from_f32<T>(X[i]);
-        } else {
-            // ============= state read-out for row block I: Y = K e^G S, Z = Q e^G S
-            const int I = I_row;
-            f32x4 accY[NVT];
-#pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) { accY[vt] = zero4(); accZ[vt] = zero4(); }
-#pragma unroll
-            for (int ks = 0; ks < DK / KS; ++ks) {
-                const int kc = ks * KS + grp * KPL;
-                typename PT::frag ak = load_frag<T>(&sm.Kr[16 * I + n16][kc]);
-                typename PT::frag aq = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
-                if (I > 0) {                                     // times e^{E_I}
-                    float xk[KPL], xq[KPL], f[KPL];
-                    PT::unpack(ak, xk);
-                    PT::unpack(aq, xq);
-                    load_f32<KPL>(f, &sm.eE[I][kc]);
-#pragma unroll
-                    for (int e = 0; e < KPL; ++e) { xk[e] *= f[e]; xq[e] *= f[e]; }
-                    ak = PT::pack(xk);
-                    aq = PT::pack(xq);
-                }
-#pragma unroll
-                for (int vt = 0; vt < NVT; ++vt) {
-                    const typename PT::frag bs = load_frag<T>(&sm.ST[16 * vt + n16][kc]);
-                    accY[vt] = PT::mma(ak, bs, accY[vt]);
-                    accZ[vt] = PT::mma(aq, bs, accZ[vt]);
-                }
-            }
-            // R = B (V - Y), stored transposed
-#pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) {
-                float rv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * I + 4 * grp + i;
-                    rv[i] = sm.beta[r] * (to_f32(sm.V[r][16 * vt + n16]) - accY[vt][i]);
-                }
-                *reinterpret_cast<QV *>(&sm.RT[16 * vt + n16][16 * I + 4 * grp]) = pack4<T>(rv);
-            }
+            for (int i = 0; i < 4; ++i)
+                rv[i] = b4[i] * (to_f32(sm.V[16 * jI + 4 * grp + i][16 * jvt + n16]) - Y[i]);
+            *reinterpret_cast<V4 *>(&sm.RT[16 * jvt + n16][16 * jI + 4 * grp]) = pack4<T>(rv);
         }
         __syncthreads();   // ---------------------------------------------- B3
         if (more) load_chunk(R, LOAD_VB, sv, t0 + C, q, k, v, g, beta, DV);
 
-        if (!state_wave) {
-            // ============= forward substitution U_I = T_II (R_I - sum_{J<I} A_IJ U_J),
-            // one value-column tile at a time; U^T overwrites R^T in place
-            for (int vt = I_row; vt < NVT; vt += 4) {
-                f32x4 X[NB], Ub[NB];
+        // ================= U: forward substitution, one wave per value tile;
+        // U^T overwrites R^T in place
+        if (wv < NVT) {
+            typedef typename PT::quad Q4;
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const int vt = wv;
+            Q4 Ub[NB];
 #pragma unroll
-                for (int I = 0; I < NB; ++I)
+            for (int I = 0; I < NB; ++I) {
+                float xr[4];
+                unpack4<T>(*reinterpret_cast<const V4 *>(&sm.RT[16 * vt + n16][16 * I + 4 * grp]), xr);
+                f32x4 X = f32x4{xr[0], xr[1], xr[2], xr[3]};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        X[I][i] = to_f32(sm.RT[16 * vt + n16][16 * I + 4 * grp + i]);
+                for (int J = 0; J < I; ++J)
+                    X = PT::mma16q(*reinterpret_cast<const Q4 *>(&sm.An[16 * I + n16][16 * J + 4 * grp]),
+                                   Ub[J], X);
+                Ub[I] = PT::to_quad(
+                    PT::mma16q(*reinterpret_cast<const Q4 *>(&sm.Tm[I][n16][4 * grp]), PT::to_quad(X),
+                               zero4()));
+            }
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
+            for (int I = 0; I < NB; ++I)
+                *reinterpret_cast<Q4 *>(&sm.RT[16 * vt + n16][16 * I + 4 * grp]) = Ub[I];
+        }
+        // (K o e^{G_n - G})^T fragments of this wave's state row tile
+        typename PT::frag kb[C / KS];
+        if (wv < Cf::NTILE) {
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const int c = 16 * ct + n16;
 #pragma unroll
-                    for (int J = 0; J < I; ++J) {
-                        float aA[4], bU[4];
+            for (int ks = 0; ks < C / KS; ++ks) {
+                const int kj = ks * KS + grp * KPL;
+                const float f = sm.eTi[kj >> 4][c];
+                float x[KPL];
+                PT::unpack(load_frag<T>(&sm.KdT[c][kj]), x);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            aA[i] = -to_f32(sm.A[16 * I + n16][16 * J + 4 * grp + i]);
-                            bU[i] = Ub[J][i];
-                        }
-                        X[I] = PT::mma16(aA, bU, X[I]);
-                    }
-                    float aT[4], bX[4] = {X[I][0], X[I][1], X[I][2], X[I][3]};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) aT[i] = to_f32(sm.Tm[I][n16][4 * grp + i]);
-                    Ub[I] = PT::mma16(aT, bX, zero4());
-                }
-#pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    float u4[4] = {Ub[I][0], Ub[I][1], Ub[I][2], Ub[I][3]};
-                    *reinterpret_cast<QV *>(&sm.RT[16 * vt + n16][16 * I + 4 * grp]) = pack4<T>(u4);
-                }
+                for (int e = 0; e < KPL; ++e) x[e] *= f;
+                kb[ks] = PT::pack(x);
             }
         }
         __syncthreads();   // ---------------------------------------------- B4
 
-        if (state_wave) {
-            // ============= S' = Diag(gamma) S + (K o e^{G_n - G})^T U
+        // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
+        if (wv < Cf::NTILE) {
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[NB][16 * ct + 4 * grp]);
 #pragma unroll
-            for (int a = 0; a < Cf::SCT; ++a) {
-                const int c = 16 * (ct0 + a) + n16;
-                typename PT::frag kb[C / KS];                    // (K o e^{G_n - G})^T
+            for (int s = 0; s < NST; ++s) {
+                const int vt = (wv + Cf::NW * s) / NCT;
+                f32x4 acc = S[s] * gam;
 #pragma unroll
                 for (int ks = 0; ks < C / KS; ++ks) {
                     const int kj = ks * KS + grp * KPL;
-                    const float f = sm.eT[kj >> 4][c];
-                    float x[KPL];
-#pragma unroll
-                    for (int e = 0; e < KPL; ++e) x[e] = to_f32(sm.Kc[kj + e][c]) * f;
-                    kb[ks] = PT::pack(x);
+                    acc = PT::mma(kb[ks], load_frag<T>(&sm.RT[16 * vt + n16][kj]), acc);
                 }
-                float gam[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gam[i] = sm.eE[NB][16 * (ct0 + a) + 4 * grp + i];
-#pragma unroll
-                for (int bq = 0; bq < Cf::SVT; ++bq) {
-                    f32x4 acc = S[a][bq];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] *= gam[i];
-#pragma unroll
-                    for (int ks = 0; ks < C / KS; ++ks) {
-                        const int kj = ks * KS + grp * KPL;
-                        acc = PT::mma(kb[ks], load_frag<T>(&sm.RT[16 * (vt0 + bq) + n16][kj]),
-                                      acc);
-                    }
-                    S[a][bq] = acc;
-                    float s4[4] = {acc[0], acc[1], acc[2], acc[3]};
-                    *reinterpret_cast<QV *>(
-                        &sm.ST[16 * (vt0 + bq) + n16][16 * (ct0 + a) + 4 * grp]) = pack4<T>(s4);
-                }
+                S[s] = acc;
+                float s4[4] = {acc[0], acc[1], acc[2], acc[3]};
+                *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
             }
-        } else {
-            // ============= O = Z + P U for row block I, written straight to o
-            const int I = I_row;
-            const int nks = (16 * (I + 1) + KS - 1) / KS;
-            T *ob = o + (t0 * H + head) * DV + sv.v0;         // wave-uniform
-#pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) {
-                f32x4 acc = accZ[vt];
-                for (int ks = 0; ks < nks; ++ks) {
-                    const int kj = ks * KS + grp * KPL;
-                    acc = PT::mma(load_frag<T>(&sm.P[16 * I + n16][kj]),
-                                  load_frag<T>(&sm.RT[16 * vt + n16][kj]), acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * I + 4 * grp + i;
-                    if (row < nvalid)
-                        ob[(uint32_t)row * (uint32_t)(H * DV) + 16 * vt + n16] =
-                            from_f32<T>(acc[i]);
-                }
+        }
+        if (has_job) {
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            // transposed block: lane holds O[16 jI + n16][16 jvt + 4 grp + i]
+            const int nks = (16 * (jI + 1) + KS - 1) / KS;
+            f32x4 acc = Zt;
+            for (int ks = 0; ks < nks; ++ks) {
+                const int kj = ks * KS + grp * KPL;
+                acc = PT::mma(load_frag<T>(&sm.RT[16 * jvt + n16][kj]),
+                              load_frag<T>(&sm.P[16 * jI + n16][kj]), acc);
+            }
+            const int row = 16 * jI + n16;
+            if (row < nvalid) {
+                T *ob = o + (t0 * H + head) * DV + sv.v0;         // wave-uniform
+                float o4[4] = {acc[0], acc[1], acc[2], acc[3]};
+                *reinterpret_cast<V4 *>(ob + (uint32_t)row * (uint32_t)(H * DV) + 16 * jvt +
+                                        4 * grp) = pack4<T>(o4);
             }
         }
         __syncthreads();   // ---------------------------------------------- B5
     }
 
-    if (sfinal && state_wave) {
+    if (sfinal) {
 #pragma unroll
-        for (int a = 0; a < Cf::SCT; ++a)
-#pragma unroll
-            for (int bq = 0; bq < Cf::SVT; ++bq)
+        for (int s = 0; s < NST; ++s) {
+            const int tl = wv + Cf::NW * s, vt = tl / NCT;
+            if (tl < Cf::NTILE) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    sfinal[sbase + (int64_t)(16 * (ct0 + a) + 4 * grp + i) * DV +
-                           16 * (vt0 + bq) + n16] = S[a][bq][i];
+                    sfinal[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16] = S[s][i];
+            }
+        }
     }
 }
 
@@ -628,9 +657,9 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 {
     const int64_t nwork = (int64_t)num_seqs * H * (D / BV);
     if (nwork == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill64_kernel<T, D, BV, D>), dim3((unsigned)nwork), dim3(512), 0,
-                       stream, (const T *)q, (const T *)k, (const T *)v, g, beta, s0, cu,
-                       num_seqs, seq_len, H, (T *)o, sf);
+    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D>), dim3((unsigned)nwork),
+                       dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)q, (const T *)k,
+                       (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (T *)o, sf);
     return hipGetLastError();
 }
 
