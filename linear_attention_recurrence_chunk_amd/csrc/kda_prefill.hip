@@ -35,9 +35,11 @@
 //
 // Work split: 16 waves, each with a fixed job in every phase of a chunk.
 //   E    all waves: decays of a (16-token sub-block, channel pair, 4 rows) item
-//        and the operand tiles K o e^L, Q o e^L, K o e^-L (and its transpose).
+//        and the operand tiles K o e^L, Q o e^L, K o e^{B-L}, K o e^-L; it runs
+//        in the previous chunk's U phase.
 //   AP   waves 0-3: diagonal block I of A and P and the inverse of I + A_II,
-//        kept in registers; waves 4-15: one off-diagonal block of A or of P.
+//        kept in registers; waves 4-9: one pair of off-diagonal blocks of A
+//        and P; waves 10-15: the decay tables and K o e^-L transposed.
 //   YZ   wave (I, value tile): (K o e^G) S and (Q o e^G) S for its 16 rows and
 //        16 value columns, then R = B (V - (K o e^G) S).
 //   U    one wave per 16 value columns: the forward substitution.
@@ -85,8 +87,9 @@ struct Smem {
     typedef Cfg<T, DK, BV> Cf;
     T Kr[Cf::C][Cf::LDK];       // K o e^{L}         row operand
     T Qr[Cf::C][Cf::LDK];       // Q o e^{L}
-    T Kd[Cf::C][Cf::LDK];       // K o e^{-L}        column operand
-    T KdT[DK][Cf::LDC];         // the same, [channel][token]
+    T Kc[Cf::C][Cf::LDK];       // K o e^{B - L}     column operand, blocks J < I
+    T Kd[Cf::C][Cf::LDK];       // K o e^{-L}        column operand, diagonal blocks
+    T KdT[DK][Cf::LDC];         // K o e^{-L}, [channel][token]
     T P[Cf::C][Cf::LDC];        // Tril((Q o e^G)(K o e^-G)^T)
     T An[Cf::C][Cf::LDC];       // -A, blocks J < I
     T Tm[Cf::NB][16][Cf::LD16]; // (I + A_II)^-1
@@ -225,50 +228,132 @@ template <typename T> __device__ __forceinline__ void unpack4(typename Vec<T>::f
 }
 
 
-// Off-diagonal block (I, J < I) of A (IS_P false; stored negated, beta
-// applied) or of P.  The column operand K o e^{-L_j} is brought to the
-// reference of row block I by prod_{J<=m<I} e^{B_m}.  The product is taken
+// Elementwise phase for one chunk: from the raw g, k, q of this thread's item
+// (sub-block I, channels 2 cp and 2 cp + 1, rows 4 qr .. 4 qr + 3 of the
+// sub-block), the sub-block-local decays and the operand tiles K o e^L,
+// Q o e^L, K o e^{B-L}, K o e^-L and e^{B_I}; then
+// this thread's share of beta and of the value slice.  FULL: every row of the
+// chunk lies in the sequence.
+template <bool FULL, typename T, int DK, int BV>
+__device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv)
+{
+    typedef Cfg<T, DK, BV> Cf;
+    typedef typename Vec<T>::two V2;
+    typedef typename Vec<T>::eight_bytes V8;
+    const int wv = wave_id();
+    if (wv < Cf::EWAVES) {
+        const int lp = opaque_lane(), n16 = lp & 15, qr = lp >> 4;
+        const int I = wv / Cf::WPB, cp = (wv % Cf::WPB) * 16 + n16;
+        const int r0 = 16 * I + 4 * qr;
+        // per channel: e^{L_r} (eL) and e^{B - L_r} (sx) for the four rows, e^{-B}
+        float eL[2][4], sx[2][4], rb[2], ebv[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            float a[4], pl[4], sl[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = (FULL || r0 + r < nv) ? __expf(R.g[r][cc]) : 1.f;
+            pl[0] = a[0];
+#pragma unroll
+            for (int r = 1; r < 4; ++r) pl[r] = pl[r - 1] * a[r];
+            sl[3] = 1.f;
+#pragma unroll
+            for (int r = 2; r >= 0; --r) sl[r] = sl[r + 1] * a[r + 1];
+            // decays of the four row quarters of this sub-block
+            float qd[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qd[j] = __shfl(pl[3], n16 + 16 * j);
+            const float lead = ((qr > 0 ? qd[0] : 1.f) * (qr > 1 ? qd[1] : 1.f)) * (qr > 2 ? qd[2] : 1.f);
+            const float tail = ((qr < 1 ? qd[1] : 1.f) * (qr < 2 ? qd[2] : 1.f)) * (qr < 3 ? qd[3] : 1.f);
+            ebv[cc] = ((qd[0] * qd[1]) * qd[2]) * qd[3];
+            rb[cc] = __builtin_amdgcn_rcpf(ebv[cc]);                 // <= e^80
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                eL[cc][r] = lead * pl[r];
+                sx[cc][r] = sl[r] * tail;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool in = FULL || r0 + r < nv;
+            float kk[2], qq[2], kc[2], kd[2];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                kk[cc] = in ? to_f32(R.k[r][cc]) : 0.f;
+                qq[cc] = in ? to_f32(R.q[r][cc]) : 0.f;
+                kc[cc] = kk[cc] * sx[cc][r];              // e^{B - L_r} <= 1
+                kd[cc] = kc[cc] * rb[cc];                 // e^{-L_r} <= e^80
+            }
+            *reinterpret_cast<V2 *>(&sm.Kr[r0 + r][2 * cp]) =
+                pack2<T>(kk[0] * eL[0][r], kk[1] * eL[1][r]);
+            *reinterpret_cast<V2 *>(&sm.Qr[r0 + r][2 * cp]) =
+                pack2<T>(qq[0] * eL[0][r], qq[1] * eL[1][r]);
+            *reinterpret_cast<V2 *>(&sm.Kc[r0 + r][2 * cp]) = pack2<T>(kc[0], kc[1]);
+            *reinterpret_cast<V2 *>(&sm.Kd[r0 + r][2 * cp]) = pack2<T>(kd[0], kd[1]);
+        }
+        if (qr == 0) *reinterpret_cast<f32x2 *>(&sm.eB[I][2 * cp]) = f32x2{ebv[0], ebv[1]};
+    }
+    const int to = 64 * wv + opaque_lane();     // threadIdx.x, recomputed
+    if (to < Cf::C) sm.beta[to] = (FULL || to < nv) ? R.beta : 0.f;   // beta = 0 masks rows past the end
+#pragma unroll
+    for (int m = 0; m < Cf::NVV; ++m) {
+        const int vi = to + Cf::NT * m;
+        const int row = vi / Cf::VPR, cv = vi % Cf::VPR;
+        if (row < Cf::C) *reinterpret_cast<V8 *>(&sm.V[row][cv * Cf::VEC]) = R.v[m];
+    }
+}
+
+template <typename T, int DK, int BV>
+__device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv)
+{
+    if (nv >= Cfg<T, DK, BV>::C) e_phase<true>(sm, R, nv);
+    else e_phase<false>(sm, R, nv);
+}
+
+// Off-diagonal blocks (I, J < I) of A (stored negated, beta applied) and of P.
+// The column operand K o e^{B_J - L_j} is brought to the reference of row
+// block I by prod_{J<m<I} e^{B_m} (nothing for adjacent blocks), once for
+// both products.  The products are taken
 // transposed so that each lane ends with four consecutive columns of one row.
-template <int I, int J, bool IS_P, typename T, int DK, int BV>
-__device__ __forceinline__ void ap_offdiag(Smem<T, DK, BV> &sm, int n16, int grp)
+template <int I, int J, typename T, int DK, int BV>
+__device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp)
 {
     typedef Path<T> PT;
     typedef typename Vec<T>::four V4;
     constexpr int KS = PT::KS, KPL = PT::KPL;
-    f32x4 acc = zero4();
+    f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
     for (int ks = 0; ks < DK / KS; ++ks) {
         const int kc = ks * KS + grp * KPL;
-        float x[KPL], f[KPL];
-        PT::unpack(load_frag<T>(&sm.Kd[16 * J + n16][kc]), x);
-        load_f32<KPL>(f, &sm.eB[J][kc]);
+        typename PT::frag col = load_frag<T>(&sm.Kc[16 * J + n16][kc]);
+        if (I > J + 1) {
+            float x[KPL], f[KPL];
+            PT::unpack(col, x);
+            load_f32<KPL>(f, &sm.eB[J + 1][kc]);
 #pragma unroll
-        for (int m = J + 1; m < I; ++m) {
-            float f2[KPL];
-            load_f32<KPL>(f2, &sm.eB[m][kc]);
+            for (int m = J + 2; m < I; ++m) {
+                float f2[KPL];
+                load_f32<KPL>(f2, &sm.eB[m][kc]);
 #pragma unroll
-            for (int e = 0; e < KPL; ++e) f[e] *= f2[e];
+                for (int e = 0; e < KPL; ++e) f[e] *= f2[e];
+            }
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) x[e] *= f[e];
+            col = PT::pack(x);
         }
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) x[e] *= f[e];
-        const typename PT::frag col = PT::pack(x);
-        const typename PT::frag row =
-            load_frag<T>(IS_P ? &sm.Qr[16 * I + n16][kc] : &sm.Kr[16 * I + n16][kc]);
-        acc = PT::mma(col, row, acc);
+        accA = PT::mma(col, load_frag<T>(&sm.Kr[16 * I + n16][kc]), accA);
+        accP = PT::mma(col, load_frag<T>(&sm.Qr[16 * I + n16][kc]), accP);
     }
     // lane holds X[r][j], r = 16 I + n16, j = 16 J + 4 grp + i
     const int r = 16 * I + n16;
-    float w[4];
-    if (IS_P) {
+    const float nb = -sm.beta[r];
+    float wa[4], wp[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = acc[i];
-        *reinterpret_cast<V4 *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(w);
-    } else {
-        const float nb = -sm.beta[r];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = nb * acc[i];
-        *reinterpret_cast<V4 *>(&sm.An[r][16 * J + 4 * grp]) = pack4<T>(w);
+    for (int i = 0; i < 4; ++i) {
+        wa[i] = nb * accA[i];
+        wp[i] = accP[i];
     }
+    *reinterpret_cast<V4 *>(&sm.An[r][16 * J + 4 * grp]) = pack4<T>(wa);
+    *reinterpret_cast<V4 *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(wp);
 }
 
 // (K o e^G) S and (Q o e^G) S for row block I and value tile vt.  The decay
@@ -299,6 +384,13 @@ __device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt, int
     }
 }
 
+// Rows of the chunk starting at t0 that lie in the sequence, at most C.
+__device__ __forceinline__ int rows_in(int64_t t0, int64_t eos, int C)
+{
+    const int64_t n = eos - t0;
+    return n < C ? (int)n : C;
+}
+
 template <typename T, int DK, int BV, int DV>
 __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -309,9 +401,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     typedef Cfg<T, DK, BV> Cf;
     typedef Path<T> PT;
     typedef Smem<T, DK, BV> Sm;
-    typedef typename Vec<T>::two V2;
     typedef typename Vec<T>::four V4;
-    typedef typename Vec<T>::eight_bytes V8;
     constexpr int C = Cf::C, NB = Cf::NB, NT = Cf::NT, KS = PT::KS, KPL = PT::KPL;
     constexpr int NSLICE = DV / BV;
     constexpr int NVT = Cf::NVT, NCT = Cf::NCT, NST = Cf::NST;
@@ -340,25 +430,27 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
 
     const int t = threadIdx.x;
     const int lane = lane_id(), wv = wave_id();
-    const int n16 = lane & 15, grp = lane >> 4;
 
     // ---- state tiles of this wave, D layout: tile (ct, vt) holds
     // S[16 ct + 4 grp + i][16 vt + n16].  Tiles wv, wv + 16, ... share one ct.
     const int ct = wv % NCT;
     f32x4 S[NST];
     const int64_t sbase = ((int64_t)seq * H + head) * (int64_t)(DK * DV) + sv.v0;
+    {
+        const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
-        S[s] = zero4();
-        const int tl = wv + Cf::NW * s, vt = tl / NCT;
-        if (tl < Cf::NTILE) {
-            if (s0) {
+        for (int s = 0; s < NST; ++s) {
+            S[s] = zero4();
+            const int tl = wv + Cf::NW * s, vt = tl / NCT;
+            if (tl < Cf::NTILE) {
+                if (s0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[s][i] = s0[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16];
+                    for (int i = 0; i < 4; ++i)
+                        S[s][i] = s0[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16];
+                }
+                float s4[4] = {S[s][0], S[s][1], S[s][2], S[s][3]};
+                *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
             }
-            float s4[4] = {S[s][0], S[s][1], S[s][2], S[s][3]};
-            *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
         }
     }
     // constant zero blocks above the diagonal of P
@@ -373,84 +465,24 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
 
     const int64_t nchunks = (sv.eos - sv.bos + C - 1) / C;
     ChunkRegs<T, DK, BV> R;
-    if (nchunks > 0) load_chunk(R, LOAD_ALL, sv, sv.bos, q, k, v, g, beta, DV);
+    if (nchunks > 0) {
+        load_chunk(R, LOAD_ALL, sv, sv.bos, q, k, v, g, beta, DV);
+        e_phase(sm, R, rows_in(sv.bos, sv.eos, C));
+    }
+    __syncthreads();
 
+    // Per chunk: AP | YZ | U and the next chunk's E | SO.  The elementwise
+    // phase of chunk c + 1 writes only tiles that chunk c no longer reads.
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = sv.bos + ch * C;
-        const int64_t nvalid = sv.eos - t0;              // rows of this chunk in the sequence
-        const bool full = nvalid >= C;
-
-        // ================= E: sub-block-local decays and operand tiles
-        if (wv < Cf::EWAVES) {
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
-            const int I = wv / Cf::WPB, cp = (wv % Cf::WPB) * 16 + n16, qr = grp;
-            const int r0 = 16 * I + 4 * qr;
-            float kr[4][2], qv[4][2], kd[4][2], ebv[2];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                float a[4], pl[4], sl[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    a[r] = (full || r0 + r < nvalid) ? __expf(R.g[r][cc]) : 1.f;
-                pl[0] = a[0];
-#pragma unroll
-                for (int r = 1; r < 4; ++r) pl[r] = pl[r - 1] * a[r];
-                sl[3] = 1.f;
-#pragma unroll
-                for (int r = 2; r >= 0; --r) sl[r] = sl[r + 1] * a[r + 1];
-                // decays of the four row quarters of this sub-block
-                float qd[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) qd[j] = __shfl(pl[3], n16 + 16 * j);
-                float lead = 1.f, tail = 1.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (j < qr) lead *= qd[j];
-                    if (j > qr) tail *= qd[j];
-                }
-                const float eb = ((qd[0] * qd[1]) * qd[2]) * qd[3];
-                const float rb = __builtin_amdgcn_rcpf(eb);     // <= e^80
-                ebv[cc] = eb;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool in = full || r0 + r < nvalid;
-                    const float kk = in ? to_f32(R.k[r][cc]) : 0.f;
-                    const float qq = in ? to_f32(R.q[r][cc]) : 0.f;
-                    const float eL = lead * pl[r];            // e^{L_r}
-                    const float sfx = sl[r] * tail;           // e^{B - L_r}
-                    kr[r][cc] = kk * eL;
-                    qv[r][cc] = qq * eL;
-                    kd[r][cc] = (kk * sfx) * rb;              // e^{-L_r}, <= e^80
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                *reinterpret_cast<V2 *>(&sm.Kr[r0 + r][2 * cp]) = pack2<T>(kr[r][0], kr[r][1]);
-                *reinterpret_cast<V2 *>(&sm.Qr[r0 + r][2 * cp]) = pack2<T>(qv[r][0], qv[r][1]);
-                *reinterpret_cast<V2 *>(&sm.Kd[r0 + r][2 * cp]) = pack2<T>(kd[r][0], kd[r][1]);
-            }
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                float c4[4] = {kd[0][cc], kd[1][cc], kd[2][cc], kd[3][cc]};
-                *reinterpret_cast<V4 *>(&sm.KdT[2 * cp + cc][r0]) = pack4<T>(c4);
-            }
-            if (qr == 0) *reinterpret_cast<f32x2 *>(&sm.eB[I][2 * cp]) = f32x2{ebv[0], ebv[1]};
-        }
-        if (t < C) sm.beta[t] = t < nvalid ? R.beta : 0.f;     // beta = 0 masks rows past the end
-#pragma unroll
-        for (int m = 0; m < Cf::NVV; ++m) {
-            const int vi = t + NT * m;
-            const int row = vi / Cf::VPR, cv = vi % Cf::VPR;
-            if (row < C) *reinterpret_cast<V8 *>(&sm.V[row][cv * Cf::VEC]) = R.v[m];
-        }
-        __syncthreads();   // ---------------------------------------------- B1
+        const int nv = rows_in(t0, sv.eos, C);           // rows of this chunk in the sequence
         const bool more = ch + 1 < nchunks;
-        if (more) load_chunk(R, LOAD_G, sv, t0 + C, q, k, v, g, beta, DV);
+        if (more) load_chunk(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, beta, DV);
 
         // ================= AP
         if (wv < NB) {
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
             // diagonal block I: A_II both ways round, P_II, then (I + A_II)^-1
+            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
             const int I = wv;
             f32x4 accAt = zero4(), accA = zero4(), accPt = zero4();
 #pragma unroll
@@ -499,24 +531,37 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             for (int i = 0; i < 4; ++i) mNd[i] = -Nd[i];
             X = PT::mma16q(PT::to_quad(mNd), PT::to_quad(X), X);  // (I - N^T)(...)
             *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(X);
-        } else if (wv < NB + 12) {
+        } else if (wv < NB + 6) {
+            // off-diagonal block pairs; the heavier (farther) ones first, so
+            // that the four SIMDs get similar shares
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
             switch (wv - NB) {
-                case 0: ap_offdiag<1, 0, false>(sm, n16, grp); break;
-                case 1: ap_offdiag<1, 0, true>(sm, n16, grp); break;
-                case 2: ap_offdiag<2, 1, false>(sm, n16, grp); break;
-                case 3: ap_offdiag<2, 1, true>(sm, n16, grp); break;
-                case 4: ap_offdiag<3, 2, false>(sm, n16, grp); break;
-                case 5: ap_offdiag<3, 2, true>(sm, n16, grp); break;
-                case 6: ap_offdiag<2, 0, false>(sm, n16, grp); break;
-                case 7: ap_offdiag<2, 0, true>(sm, n16, grp); break;
-                case 8: ap_offdiag<3, 1, false>(sm, n16, grp); break;
-                case 9: ap_offdiag<3, 1, true>(sm, n16, grp); break;
-                case 10: ap_offdiag<3, 0, false>(sm, n16, grp); break;
-                default: ap_offdiag<3, 0, true>(sm, n16, grp); break;
+                case 0: ap_pair<3, 0>(sm, n16, grp); break;
+                case 1: ap_pair<2, 0>(sm, n16, grp); break;
+                case 2: ap_pair<3, 1>(sm, n16, grp); break;
+                case 3: ap_pair<1, 0>(sm, n16, grp); break;
+                case 4: ap_pair<2, 1>(sm, n16, grp); break;
+                default: ap_pair<3, 2>(sm, n16, grp); break;
             }
-            // decay tables, one channel per thread
-            const int c = t - 64 * NB;
+        } else {
+            // decay tables, one channel per thread; then K o e^-L transposed,
+            // for the state update (two channels by four tokens per task)
+            typedef typename Vec<T>::two V2;
+            const int tw = 64 * (wv - NB - 6) + opaque_lane();
+            const int c = tw;
+            for (int task = tw; task < (DK / 2) * (C / 4); task += 64 * (Cf::NW - NB - 6)) {
+                const int cpair = task % (DK / 2), tq = task / (DK / 2);
+                float x[2][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const V2 d2 = *reinterpret_cast<const V2 *>(&sm.Kd[4 * tq + r][2 * cpair]);
+                    x[0][r] = to_f32(d2[0]);
+                    x[1][r] = to_f32(d2[1]);
+                }
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
+                    *reinterpret_cast<V4 *>(&sm.KdT[2 * cpair + cc][4 * tq]) = pack4<T>(x[cc]);
+            }
             if (c < DK) {
                 float e[NB];
 #pragma unroll
@@ -535,8 +580,8 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 }
             }
         }
-        __syncthreads();   // ---------------------------------------------- B2
-        if (more) load_chunk(R, LOAD_KQ, sv, t0 + C, q, k, v, g, beta, DV);
+        __syncthreads();   // ---------------------------------------------- B1
+        if (more) load_chunk(R, LOAD_VB, sv, t0 + C, q, k, v, g, beta, DV);
 
         // ================= YZ: state read-out and R = B (V - Y), stored transposed
         f32x4 Zt = zero4();
@@ -552,8 +597,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 rv[i] = b4[i] * (to_f32(sm.V[16 * jI + 4 * grp + i][16 * jvt + n16]) - Y[i]);
             *reinterpret_cast<V4 *>(&sm.RT[16 * jvt + n16][16 * jI + 4 * grp]) = pack4<T>(rv);
         }
-        __syncthreads();   // ---------------------------------------------- B3
-        if (more) load_chunk(R, LOAD_VB, sv, t0 + C, q, k, v, g, beta, DV);
+        __syncthreads();   // ---------------------------------------------- B2
 
         // ================= U: forward substitution, one wave per value tile;
         // U^T overwrites R^T in place
@@ -579,27 +623,29 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             for (int I = 0; I < NB; ++I)
                 *reinterpret_cast<Q4 *>(&sm.RT[16 * vt + n16][16 * I + 4 * grp]) = Ub[I];
         }
-        // (K o e^{G_n - G})^T fragments of this wave's state row tile
-        typename PT::frag kb[C / KS];
-        if (wv < Cf::NTILE) {
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
-            const int c = 16 * ct + n16;
-#pragma unroll
-            for (int ks = 0; ks < C / KS; ++ks) {
-                const int kj = ks * KS + grp * KPL;
-                const float f = sm.eTi[kj >> 4][c];
-                float x[KPL];
-                PT::unpack(load_frag<T>(&sm.KdT[c][kj]), x);
-#pragma unroll
-                for (int e = 0; e < KPL; ++e) x[e] *= f;
-                kb[ks] = PT::pack(x);
-            }
-        }
-        __syncthreads();   // ---------------------------------------------- B4
+        // ================= the next chunk's elementwise phase (the substituting
+        // waves do their share after their substitution)
+        if (more) e_phase(sm, R, rows_in(t0 + C, sv.eos, C));
+        __syncthreads();   // ---------------------------------------------- B3
 
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
         if (wv < Cf::NTILE) {
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            // (K o e^{G_n - G})^T fragments of this wave's state row tile
+            typename PT::frag kb[C / KS];
+            {
+                const int c = 16 * ct + n16;
+#pragma unroll
+                for (int ks = 0; ks < C / KS; ++ks) {
+                    const int kj = ks * KS + grp * KPL;
+                    const float f = sm.eTi[kj >> 4][c];
+                    float x[KPL];
+                    PT::unpack(load_frag<T>(&sm.KdT[c][kj]), x);
+#pragma unroll
+                    for (int e = 0; e < KPL; ++e) x[e] *= f;
+                    kb[ks] = PT::pack(x);
+                }
+            }
             const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[NB][16 * ct + 4 * grp]);
 #pragma unroll
             for (int s = 0; s < NST; ++s) {
@@ -626,17 +672,18 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                               load_frag<T>(&sm.P[16 * jI + n16][kj]), acc);
             }
             const int row = 16 * jI + n16;
-            if (row < nvalid) {
+            if (row < nv) {
                 T *ob = o + (t0 * H + head) * DV + sv.v0;         // wave-uniform
                 float o4[4] = {acc[0], acc[1], acc[2], acc[3]};
                 *reinterpret_cast<V4 *>(ob + (uint32_t)row * (uint32_t)(H * DV) + 16 * jvt +
                                         4 * grp) = pack4<T>(o4);
             }
         }
-        __syncthreads();   // ---------------------------------------------- B5
+        __syncthreads();   // ---------------------------------------------- B4
     }
 
     if (sfinal) {
+        const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
         for (int s = 0; s < NST; ++s) {
             const int tl = wv + Cf::NW * s, vt = tl / NCT;
