@@ -11,10 +11,12 @@
 // The state is read once and written once: the step is bound by HBM bandwidth
 // ("Glossaire", entry "Decode"), 8 d_k d_v bytes per (request, head).
 //
-// Mapping: one 256-thread workgroup per (request, head).  Thread t owns four
-// consecutive columns (one 16-byte vector) of rows r0, r0 + RPP, ...; a wave
-// therefore reads whole 512-byte rows, fully coalesced, and keeps its share of
-// S in registers between the read and the write.
+// Mapping: 256-thread workgroups step through the (request, head) items with
+// a grid stride.  Thread t owns four consecutive columns (one 16-byte vector)
+// of rows r0, r0 + RPP, ...; a wave therefore reads whole rows, fully
+// coalesced, and keeps its share of S in registers between the read and the
+// write.  The next item's state is loaded while the current one is finished,
+// so that every wave always has a state read in flight.
 #include "kda_common.hpp"
 
 namespace kda {
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
                                                      const float *__restrict__ g,
                                                      const float *__restrict__ beta,
                                                      float *__restrict__ state,
-                                                     T *__restrict__ o)
+                                                     T *__restrict__ o, int64_t NH)
 {
     constexpr int NT = 256;
     constexpr int TPR = DV / 4;        // threads per state row
@@ -34,87 +36,109 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
     constexpr int NPASS = DK / RPP;    // passes over the rows
     static_assert(DK % RPP == 0 && NPASS >= 1, "shape");
 
-    const int64_t nh = blockIdx.x;     // request * H + head
     const int t = threadIdx.x;
     const int col = (t % TPR) * 4;
     const int r0 = t / TPR;
-
-    float *S = state + nh * (int64_t)(DK * DV);
-    f32x4 s[NPASS];
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p)
-        s[p] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4 *>(S + (int64_t)(r0 + p * RPP) * DV + col));
 
     __shared__ float sq[DK], sk[DK], sa[DK];
     __shared__ f32x4 ry[RPP][TPR], rz[RPP][TPR];
     __shared__ float su[DV];
     __shared__ float sqk;
 
-    for (int c = t; c < DK; c += NT) {
-        sq[c] = to_f32(q[nh * DK + c]);
-        sk[c] = to_f32(k[nh * DK + c]);
-        sa[c] = __expf(g[nh * DK + c]);
-    }
-    __syncthreads();
-
-    if (t < 64) {  // q . k on wave 0
-        float acc = 0.f;
-        for (int c = t; c < DK; c += 64) acc += sq[c] * sk[c];
+    int64_t nh = blockIdx.x;           // request * H + head
+    f32x4 s[NPASS];
+    if (nh < NH) {
+        const float *S = state + nh * (int64_t)(DK * DV);
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-        if (t == 0) sqk = acc;
+        for (int p = 0; p < NPASS; ++p)
+            s[p] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4 *>(S + (int64_t)(r0 + p * RPP) * DV + col));
     }
-
-    f32x4 y = zero4(), z = zero4();
+    for (; nh < NH; nh += gridDim.x) {
+        float *S = state + nh * (int64_t)(DK * DV);
+        const int64_t nx = nh + gridDim.x;
+        f32x4 sn[NPASS];
+        if (nx < NH) {
+            const float *Sn = state + nx * (int64_t)(DK * DV);
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int c = r0 + p * RPP;
-        const float a = sa[c];
-        const float ka = sk[c] * a, qa = sq[c] * a;
-        y += ka * s[p];
-        z += qa * s[p];
-    }
-    ry[r0][t % TPR] = y;
-    rz[r0][t % TPR] = z;
-    __syncthreads();
-
-    if (t < TPR) {
-        f32x4 yy = zero4(), zz = zero4();
-        for (int r = 0; r < RPP; ++r) { yy += ry[r][t]; zz += rz[r][t]; }
-        const float b = beta[nh];
-        const float qk = sqk;
-        const T *vr = v + nh * DV + col;
-        float ov[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float u = b * (to_f32(vr[i]) - yy[i]);
-            su[col + i] = u;
-            ov[i] = zz[i] + qk * u;
+            for (int p = 0; p < NPASS; ++p)
+                sn[p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4 *>(Sn + (int64_t)(r0 + p * RPP) * DV + col));
         }
-        T *orow = o + nh * DV + col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) orow[i] = from_f32<T>(ov[i]);
-    }
-    __syncthreads();
 
-    const f32x4 u4 = f32x4{su[col], su[col + 1], su[col + 2], su[col + 3]};
+        for (int c = t; c < DK; c += NT) {
+            sq[c] = to_f32(q[nh * DK + c]);
+            sk[c] = to_f32(k[nh * DK + c]);
+            sa[c] = __expf(g[nh * DK + c]);
+        }
+        __syncthreads();
+
+        if (t < 64) {  // q . k on wave 0
+            float acc = 0.f;
+            for (int c = t; c < DK; c += 64) acc += sq[c] * sk[c];
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int c = r0 + p * RPP;
-        const f32x4 ns = sa[c] * s[p] + sk[c] * u4;
-        __builtin_nontemporal_store(
-            ns, reinterpret_cast<f32x4 *>(S + (int64_t)(r0 + p * RPP) * DV + col));
+            for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+            if (t == 0) sqk = acc;
+        }
+
+        f32x4 y = zero4(), z = zero4();
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int c = r0 + p * RPP;
+            const float a = sa[c];
+            const float ka = sk[c] * a, qa = sq[c] * a;
+            y += ka * s[p];
+            z += qa * s[p];
+        }
+        ry[r0][t % TPR] = y;
+        rz[r0][t % TPR] = z;
+        __syncthreads();
+
+        if (t < TPR) {
+            f32x4 yy = zero4(), zz = zero4();
+            for (int r = 0; r < RPP; ++r) { yy += ry[r][t]; zz += rz[r][t]; }
+            const float b = beta[nh];
+            const float qk = sqk;
+            const T *vr = v + nh * DV + col;
+            float ov[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float u = b * (to_f32(vr[i]) - yy[i]);
+                su[col + i] = u;
+                ov[i] = zz[i] + qk * u;
+            }
+            T *orow = o + nh * DV + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) orow[i] = from_f32<T>(ov[i]);
+        }
+        __syncthreads();
+
+        const f32x4 u4 = f32x4{su[col], su[col + 1], su[col + 2], su[col + 3]};
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int c = r0 + p * RPP;
+            const f32x4 ns = sa[c] * s[p] + sk[c] * u4;
+            __builtin_nontemporal_store(
+                ns, reinterpret_cast<f32x4 *>(S + (int64_t)(r0 + p * RPP) * DV + col));
+        }
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) s[p] = sn[p];
+        __syncthreads();   // the shared arrays are reused by the next item
     }
 }
+
+// Enough workgroups to fill the chip several times over (256 CUs), few
+// enough that each steps through several items and overlaps their reads.
+constexpr int64_t kDecodeMaxBlocks = 4096;
 
 template <typename T, int D>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, float *state, void *o, int64_t NH,
                                   hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_kernel<T, D, D>), dim3((unsigned)NH), dim3(256), 0, stream,
-                       (const T *)q, (const T *)k, (const T *)v, g, beta, state, (T *)o);
+    const int64_t blocks = NH < kDecodeMaxBlocks ? NH : kDecodeMaxBlocks;
+    hipLaunchKernelGGL((decode_kernel<T, D, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const T *)q, (const T *)k, (const T *)v, g, beta, state, (T *)o, NH);
     return hipGetLastError();
 }
 
