@@ -14,6 +14,11 @@ Two independent implementations live here:
   M_t = (I - beta_t k_t k_t^T) Diag(alpha_t) of the page "Notations
   mathematiques" (table "Attention et KDA", row M_t).  It is only for tiny
   shapes and serves to cross-check the C code.
+* ``layer_ref.py`` holds the steps around the recurrence in a KDA layer, in
+  numpy float64: L2Norm of q and k, the bounded gate that turns decay logits
+  into g, the causal ShortConv with its streaming state, RMSNorm and the
+  sigmoid output gate, and the segment summaries (transition product, state
+  from zero) with their composition.
 
 The recurrence (same page and table, rows S_t, alpha_t, g_t, o~_t):
     S_t = M_t S_{t-1} + beta_t k_t v_t^T,   alpha_t = exp(g_t),   o_t = S_t^T q_t.
