@@ -51,6 +51,121 @@ def decode_bytes(N, H, dk, dv, e_in, e_out):
     return N * H * (8 * dk * dv + e_in * (2 * dk + dv) + 4 * dk + 4 + e_out * dv)
 
 
+def fused_prefill_bytes(n_tok, n_seq, H, dk, dv, e, has_s0, has_sf):
+    """kda_chunk_fwd_fused: raw q, k and decay logits z in the input type
+    instead of normalised q, k and fp32 g (plus the per-head gate parameters)."""
+    return (n_tok * H * (e * (3 * dk + dv) + 4 + e * dv) + H * (4 + 4 * dk)
+            + n_seq * H * dk * dv * 4 * (int(has_s0) + int(has_sf)))
+
+
+def _gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def bench_layer(args, w, x, torch, kda, inputs, dev):
+    """The layer steps around the recurrence, each on the prefill workload's
+    shapes, plus the nano-K3 prefill and decode: one JSON object."""
+    res = {}
+    li = inputs.layer_inputs(w, seed=3, device=dev)
+    n_tok, n_seq = int(x["q"].shape[0]), len(x["seqlens"])
+    e = x["q"].element_size()
+    # fused front end (L2Norm of q, k and the bounded gate in the prefill kernel)
+    o = x["v"].clone()                      # stands in for a raw output below
+
+    def fstep():
+        kda.chunk_fwd_fused(li["q_raw"], li["k_raw"], x["v"], li["z"], li["A_log"], li["b_alpha"],
+                            x["beta"], x["initial_state"], x["cu_seqlens"], chunk_size=w.chunk)
+
+    ms, _ = time_launches(fstep, args.steps, args.warmup, torch)
+    fb = fused_prefill_bytes(n_tok, n_seq, w.H, w.dk, w.dv, e, x["initial_state"] is not None, True)
+    res["prefill_fused_prologue"] = {
+        "workload": w.name, "ms_per_step": ms, "tokens/s": n_tok / (ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": _gbs(fb, ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": _gbs(fb, ms) / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda::prefill_kernel<..., fused prologue>", "bytes_per_launch": fb}}
+    # output epilogue on the prefill's output rows
+    rows = n_tok * w.H
+    og = torch.empty_like(o)
+    ms, _ = time_launches(lambda: kda.output_gate(o, li["gate"], li["rms_weight"], out=og),
+                          args.steps, args.warmup, torch)
+    ob = rows * w.dv * 3 * e + 4 * w.dv
+    res["output_gate"] = {"rows": rows, "d_v": w.dv, "ms_per_step": ms, "GB/s": _gbs(ob, ms),
+                          "roofline": {"bound": "hbm", "achieved": _gbs(ob, ms),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": _gbs(ob, ms) / HBM_PEAK_GBS, "traffic": None,
+                                       "kernel": "kda::output_gate_kernel",
+                                       "bytes_per_launch": ob}}
+    # ShortConv over one projection (H * d_k channels), with streaming state
+    xc = li["k_raw"].view(n_tok, w.H * w.dk)
+    st = torch.zeros(n_seq, 3, w.H * w.dk, device=dev)
+    ms, _ = time_launches(lambda: kda.short_conv(xc, li["conv_w"], x["cu_seqlens"], st),
+                          args.steps, args.warmup, torch)
+    cb = n_tok * w.H * w.dk * 2 * e + w.H * w.dk * 16 + n_seq * 3 * w.H * w.dk * 8
+    res["short_conv"] = {"tokens": n_tok, "channels": w.H * w.dk, "ms_per_step": ms,
+                         "GB/s": _gbs(cb, ms),
+                         "roofline": {"bound": "hbm", "achieved": _gbs(cb, ms),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": _gbs(cb, ms) / HBM_PEAK_GBS, "traffic": None,
+                                      "kernel": "kda::short_conv_kernel (+ state update)",
+                                      "bytes_per_launch": cb}}
+    del li, o, og, xc, st
+    # segment summaries of the prefill sequence split in 4, and their scan
+    cu = x["cu_seqlens"]
+    if n_seq == 1:
+        T = n_tok
+        cuts = torch.tensor([0, T // 4, T // 2, 3 * T // 4, T], dtype=torch.int32, device=dev)
+        M, St = kda.kcp_summaries(x["q"], x["k"], x["v"], x["g"], x["beta"], cuts)
+        ms_sum, _ = time_launches(lambda: kda.kcp_summaries(x["q"], x["k"], x["v"], x["g"],
+                                                            x["beta"], cuts), 3, 1, torch)
+        ms_scan, _ = time_launches(lambda: kda.kcp_scan(M, St), args.steps, args.warmup, torch)
+        cnt = w.H
+        out = torch.empty_like(St[0])
+        ms_c, _ = time_launches(lambda: kda.state_compose(M[0], St[0], St[1], out=out),
+                                args.steps, args.warmup, torch)
+        d = w.dk
+        res["kcp"] = {"segments": 4, "summaries_ms": ms_sum, "scan_ms": ms_scan,
+                      "compose": {"count": cnt, "ms": ms_c,
+                                  "TFLOP/s": 2 * d ** 3 * cnt / (ms_c * 1e-3) / 1e12,
+                                  "GB/s": _gbs(4 * d * d * 4 * cnt, ms_c),
+                                  "roofline": {"bound": "hbm", "achieved": _gbs(4 * d * d * 4 * cnt, ms_c),
+                                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                               "frac": _gbs(4 * d * d * 4 * cnt, ms_c) / HBM_PEAK_GBS,
+                                               "traffic": None, "kernel": "kda::compose_kernel",
+                                               "bytes_per_launch": 4 * d * d * 4 * cnt}}}
+        del M, St, out
+    # nano-K3 shapes
+    wn = inputs.WORKLOADS["nano_k3_prefill"]
+    xn = inputs.prefill_inputs(wn, seed=2, device=dev)
+    nt, ns = int(xn["q"].shape[0]), len(xn["seqlens"])
+    on = torch.empty_like(xn["v"])
+    sfn = torch.empty((ns, wn.H, wn.dk, wn.dv), dtype=torch.float32, device=dev)
+    ms, _ = time_launches(lambda: kda.chunk_fwd(xn["q"], xn["k"], xn["v"], xn["g"], xn["beta"],
+                                                None, xn["cu_seqlens"], out=on, final_state=sfn),
+                          args.steps, args.warmup, torch)
+    nb = prefill_bytes(nt, ns, wn.H, wn.dk, wn.dv, e, e, False, True)
+    res["nano_k3_prefill"] = {"workload": wn.name, "tokens": nt, "ms_per_step": ms,
+                              "tokens/s": nt / (ms * 1e-3),
+                              "roofline": {"bound": "hbm", "achieved": _gbs(nb, ms),
+                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": _gbs(nb, ms) / HBM_PEAK_GBS, "traffic": None,
+                                           "kernel": "kda::prefill_kernel<bf16, 64, 64>",
+                                           "bytes_per_launch": nb}}
+    del xn, on, sfn
+    wd = inputs.WORKLOADS["nano_k3_decode"]
+    xd = inputs.decode_inputs(wd, seed=5, device=dev)
+    od = torch.empty_like(xd["v"])
+    ms, _ = time_launches(lambda: kda.step_decode(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"],
+                                                  xd["state"], out=od), args.steps, args.warmup, torch)
+    db = decode_bytes(wd.decode_requests, wd.H, wd.dk, wd.dv, e, e)
+    res["nano_k3_decode"] = {"workload": wd.name, "ms_per_step": ms, "GB/s": _gbs(db, ms),
+                             "roofline": {"bound": "hbm", "achieved": _gbs(db, ms),
+                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": _gbs(db, ms) / HBM_PEAK_GBS, "traffic": None,
+                                          "kernel": "kda::decode_kernel<bf16, 64>",
+                                          "bytes_per_launch": db}}
+    return res
+
+
 def _source_sha(name):
     p = os.path.join(ROOT, "linear_attention_recurrence_chunk_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
@@ -123,6 +238,9 @@ def main():
     ap.add_argument("--decode-workload", default="k3_decode_256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the layer steps (fused front end, output gate, ShortConv, "
+                         "segment composition) and the nano-K3 shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (to scale HBM counters)")
     args = ap.parse_args()
@@ -204,6 +322,9 @@ def main():
                                                     "kernel": "kda::decode_kernel",
                                                     "bytes_per_launch": dbytes}}
         del xd
+
+    if not args.no_layer:
+        out["layer"] = bench_layer(args, w, x, torch, kda, inputs, dev)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()

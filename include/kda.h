@@ -119,6 +119,93 @@ kda_status kda_step_decode(const void *q, const void *k, const void *v, const fl
                            const float *beta, float *state, void *o, int32_t N, int32_t H,
                            int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream);
 
+/*
+ * Chunkwise prefill with the layer's front end fused in: the same operation as
+ * kda_chunk_fwd, on inputs taken one step earlier in the KDA layer.
+ *   - q = L2Norm(q_raw), k = L2Norm(k_raw) per (token, head) over d_k (page
+ *     "Notations mathematiques": rows q_t, k_t "L2-normalised" and the
+ *     function table's L2Norm(x) = x / ||x||_2; a zero row stays zero);
+ *   - g = g_min sigma(e^{A_h} (z + b_alpha^h)), g_min = -5 ("Glossaire", entry
+ *     "Decroissance bornee"; notation table rows A_h, b_alpha^h, z_t).  The bias
+ *     is added to the logit before the per-head scale e^{A_h}.
+ *
+ *   q_raw, k_raw  [total_tokens][H][d_k]  dtype   unnormalised queries, keys
+ *   z             [total_tokens][H][d_k]  dtype   decay logits (replace g)
+ *   A_log         [H]        fp32                  per-head log scale A_h
+ *   b_alpha       [H][d_k]   fp32                  per-head decay bias
+ * All other arguments, the layouts, sizes, ownership, aliasing and errors are
+ * those of kda_chunk_fwd.  The g stream shrinks from 4 to 2 bytes per element
+ * (bf16 logits), and no separate normalisation pass is needed.
+ */
+kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void *v, const void *z,
+                               const float *A_log, const float *b_alpha, const float *beta,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
+                               int32_t d_v, int32_t chunk_size, kda_dtype dtype, void *o,
+                               float *final_state, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Output epilogue of the KDA layer: out = RMSNorm(o~) (.) sigma(gate), per row
+ * (token, head) over d_v, RMSNorm(x) = x / sqrt(mean(x^2) + eps) (.) weight
+ * (page "Notations mathematiques": row o~_t "raw output, before the gate" and
+ * the function table's RMSNorm; "Kimi K3" model tables: epsilon 1e-5 and a
+ * full-rank KDA output gate, i.e. one gate logit per output channel).
+ *
+ *   o_raw  [rows][d_v] dtype   the raw output (the o of kda_chunk_fwd or
+ *                              kda_step_decode, rows = tokens * H)
+ *   gate   [rows][d_v] dtype   gate logits
+ *   weight [d_v] fp32          RMSNorm weight, shared by the heads
+ *   eps    >= 0                RMSNorm epsilon
+ *   out    [rows][d_v] dtype   may alias o_raw (each element is read before
+ *                              it is written by the same thread)
+ * d_v in {32, 64, 128}.  Device pointers, 16-byte aligned; host validation as
+ * for the other calls.
+ */
+kda_status kda_output_gate(const void *o_raw, const void *gate, const float *weight, float eps,
+                           void *out, int64_t rows, int32_t d_v, kda_dtype dtype,
+                           hipStream_t stream);
+
+/*
+ * ShortConv: causal depthwise convolution with 4 taps over each packed
+ * sequence ("Notations mathematiques", function table "ShortConv"; "Glossaire",
+ * entry "ShortConv"; "Kimi K3" model table: kernel 4).  No activation.
+ *     y_t[c] = sum_{i=0..3} weight[c][i] * x_{t-3+i}[c],
+ * where inputs before the sequence start come from conv_state or are zero.
+ *
+ *   x           [total_tokens][channels] dtype
+ *   weight      [channels][4] fp32     tap 3 multiplies the current token
+ *   cu_seqlens  as in kda_chunk_fwd (device, or NULL for equal lengths)
+ *   conv_state  [num_seqs][3][channels] fp32 or NULL.  In: the three inputs
+ *               before each sequence, oldest first.  Out: the last three
+ *               inputs of each sequence (the entering ones kept in front when
+ *               a sequence is shorter than three tokens).  NULL: zero history,
+ *               nothing written.  A decode step is a call with num_seqs
+ *               sequences of one token each.
+ *   y           [total_tokens][channels] dtype; must not alias x.
+ * channels must be a multiple of 4.  Two launches on `stream` (the output,
+ * then the state update).
+ */
+kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_tokens, int32_t channels,
+                          float *conv_state, void *y, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * Composition of context-parallel segment summaries ("Glossaire", entry
+ * "KCP"; notation table rows M_t and S~): for b < count,
+ *     S_out[b] = M[b] S_in[b] + S_tilde[b]      (fp32 throughout).
+ * M[b] is the product of a segment's transitions, obtained with kda_chunk_fwd
+ * by running the segment from initial_state = I with v = 0 (so d_v = d_k);
+ * S_tilde[b] is the segment's final state from S = 0.
+ *
+ *   M        [count][d_k][d_k]     S_in, S_tilde, S_out   [count][d_k][d_v]
+ * d_k == d_v in {32, 64, 128}.  S_out must not alias M or S_in; it may alias
+ * S_tilde.
+ */
+kda_status kda_state_compose(const float *M, const float *S_in, const float *S_tilde,
+                             float *S_out, int64_t count, int32_t d_k, int32_t d_v,
+                             hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(kda_status status);
 

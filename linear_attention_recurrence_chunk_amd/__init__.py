@@ -3,15 +3,20 @@
 The compute lives in ``libkda.so`` (hand-written HIP kernels behind the C ABI
 declared in ``include/kda.h``).  This package only marshals arguments:
 ``chunk_fwd`` (prefill over packed sequences) and ``step_decode`` (one token
-per request).  The library is loaded on first use and its absence is an error.
+per request), plus the layer steps around them: ``chunk_fwd_fused`` (prefill
+with L2Norm and the bounded gate in the kernel), ``output_gate``,
+``short_conv``, ``state_compose`` and the segment helpers ``kcp_summaries`` /
+``kcp_scan``.  The library is loaded on first use and its absence is an error.
 """
 from . import inputs  # noqa: F401  (seeded synthetic inputs; no compute)
 
-__all__ = ["chunk_fwd", "step_decode", "inputs", "library"]
+_API = ("chunk_fwd", "step_decode", "chunk_fwd_fused", "output_gate", "short_conv",
+        "state_compose", "kcp_summaries", "kcp_scan", "library", "workspace_size", "KdaError")
+__all__ = list(_API[:8]) + ["inputs", "library"]
 
 
 def __getattr__(name):
-    if name in ("chunk_fwd", "step_decode", "library", "workspace_size", "KdaError"):
+    if name in _API:
         from . import _lib
         return getattr(_lib, name)
     raise AttributeError(name)

@@ -47,6 +47,15 @@ def library() -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = i32
     lib.kda_step_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_step_decode.restype = i32
+    lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                        i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_fused.restype = i32
+    lib.kda_output_gate.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i32, i32, vp]
+    lib.kda_output_gate.restype = i32
+    lib.kda_short_conv.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, i32, vp]
+    lib.kda_short_conv.restype = i32
+    lib.kda_state_compose.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
+    lib.kda_state_compose.restype = i32
     lib.kda_status_string.argtypes = [i32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -177,3 +186,156 @@ def step_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
                                    _ptr(out), N, H, dk, dv, _DTYPES[q.dtype], _stream(dev))
     _check("kda_step_decode", st)
     return out
+
+
+def _layout(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor]):
+    """(num_seqs, n_tok) of packed 3-D or batched 4-D token-major inputs."""
+    if q.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens is only accepted with packed 3-D inputs")
+        return q.shape[0], q.shape[0] * q.shape[1]
+    if cu_seqlens is None:
+        return 1, q.shape[0]
+    _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=(1,), device=q.device)
+    return cu_seqlens.shape[0] - 1, q.shape[0]
+
+
+def chunk_fwd_fused(q_raw: torch.Tensor, k_raw: torch.Tensor, v: torch.Tensor, z: torch.Tensor,
+                    A_log: torch.Tensor, b_alpha: torch.Tensor, beta: torch.Tensor,
+                    initial_state: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                    output_final_state: bool = True
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill with the fused front end (kda_chunk_fwd_fused): q, k are
+    L2-normalised in the kernel and g = -5 sigma(e^{A_h} (z + b_alpha^h)).
+    q_raw, k_raw, z like q of chunk_fwd (same dtype); A_log [H] fp32;
+    b_alpha [H, d_k] fp32; the rest as chunk_fwd."""
+    if q_raw.dtype not in _DTYPES:
+        raise ValueError(f"q_raw must be bf16 or fp32, got {q_raw.dtype}")
+    dev = q_raw.device
+    _need(q_raw, "q_raw", ndim=(3, 4))
+    for name, x in (("k_raw", k_raw), ("v", v), ("z", z)):
+        _need(x, name, dtype=q_raw.dtype, ndim=(q_raw.dim(),), device=dev)
+    _need(beta, "beta", dtype=torch.float32, ndim=(q_raw.dim() - 1,), device=dev)
+    num_seqs, n_tok = _layout(q_raw, cu_seqlens)
+    H, dk = q_raw.shape[-2:]
+    dv = v.shape[-1]
+    if k_raw.shape != q_raw.shape or z.shape != q_raw.shape or v.shape[:-1] != q_raw.shape[:-1]:
+        raise ValueError("q_raw, k_raw, z must share a shape and v must match it up to d_v")
+    if beta.shape != q_raw.shape[:-1]:
+        raise ValueError(f"beta must have shape {tuple(q_raw.shape[:-1])}")
+    _need(A_log, "A_log", dtype=torch.float32, ndim=(1,), device=dev)
+    _need(b_alpha, "b_alpha", dtype=torch.float32, ndim=(2,), device=dev)
+    if tuple(A_log.shape) != (H,) or tuple(b_alpha.shape) != (H, dk):
+        raise ValueError("A_log must be [H] and b_alpha [H, d_k]")
+    sshape = (num_seqs, H, dk, dv)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dtype=torch.float32, device=dev)
+        if tuple(initial_state.shape) != sshape:
+            raise ValueError(f"initial_state must have shape {sshape}")
+    out = torch.empty_like(v)
+    final_state = torch.empty(sshape, dtype=torch.float32, device=dev) if output_final_state else None
+    st = library().kda_chunk_fwd_fused(
+        _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(z), _ptr(A_log), _ptr(b_alpha), _ptr(beta),
+        _ptr(initial_state), _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv, chunk_size,
+        _DTYPES[q_raw.dtype], _ptr(out), _ptr(final_state), None, 0, _stream(dev))
+    _check("kda_chunk_fwd_fused", st)
+    return out, final_state
+
+
+def output_gate(o_raw: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor,
+                eps: float = 1e-5, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """RMSNorm(o_raw) * sigmoid(gate) over the last axis (kda_output_gate)."""
+    if o_raw.dtype not in _DTYPES:
+        raise ValueError(f"o_raw must be bf16 or fp32, got {o_raw.dtype}")
+    dev = o_raw.device
+    _need(o_raw, "o_raw")
+    _need(gate, "gate", dtype=o_raw.dtype, device=dev)
+    _need(weight, "weight", dtype=torch.float32, ndim=(1,), device=dev)
+    dv = o_raw.shape[-1]
+    if gate.shape != o_raw.shape or tuple(weight.shape) != (dv,):
+        raise ValueError("gate must match o_raw and weight must be [d_v]")
+    if out is None:
+        out = torch.empty_like(o_raw)
+    st = library().kda_output_gate(_ptr(o_raw), _ptr(gate), _ptr(weight), float(eps), _ptr(out),
+                                   o_raw.numel() // dv, dv, _DTYPES[o_raw.dtype], _stream(dev))
+    _check("kda_output_gate", st)
+    return out
+
+
+def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+               conv_state: Optional[torch.Tensor] = None, num_seqs: Optional[int] = None
+               ) -> torch.Tensor:
+    """Causal 4-tap depthwise convolution (kda_short_conv).  x [N_tok, C]
+    (packed; one sequence, ``num_seqs`` equal ones, or cu_seqlens); weight
+    [C, 4] fp32; conv_state [N, 3, C] fp32 is read and updated in place."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"x must be bf16 or fp32, got {x.dtype}")
+    dev = x.device
+    _need(x, "x", ndim=(2,))
+    _need(weight, "weight", dtype=torch.float32, ndim=(2,), device=dev)
+    n_tok, C = x.shape
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=(1,), device=dev)
+        nseq = cu_seqlens.shape[0] - 1
+    else:
+        nseq = 1 if num_seqs is None else int(num_seqs)
+    if tuple(weight.shape) != (C, 4):
+        raise ValueError("weight must be [C, 4]")
+    if conv_state is not None:
+        _need(conv_state, "conv_state", dtype=torch.float32, device=dev)
+        if tuple(conv_state.shape) != (nseq, 3, C):
+            raise ValueError(f"conv_state must be {(nseq, 3, C)}")
+    y = torch.empty_like(x)
+    st = library().kda_short_conv(_ptr(x), _ptr(weight), _ptr(cu_seqlens), nseq, n_tok, C,
+                                  _ptr(conv_state), _ptr(y), _DTYPES[x.dtype], _stream(dev))
+    _check("kda_short_conv", st)
+    return y
+
+
+def state_compose(M: torch.Tensor, S_in: torch.Tensor, S_tilde: torch.Tensor,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """S_out = M @ S_in + S_tilde over a batch of fp32 matrices (kda_state_compose)."""
+    dev = M.device
+    for name, x in (("M", M), ("S_in", S_in), ("S_tilde", S_tilde)):
+        _need(x, name, dtype=torch.float32, device=dev)
+    d = M.shape[-1]
+    if M.shape[-2] != d or S_in.shape != S_tilde.shape or S_in.shape[:-2] != M.shape[:-2] \
+            or S_in.shape[-2] != d:
+        raise ValueError("M must be [..., d, d] and S_in, S_tilde [..., d, d_v]")
+    if out is None:
+        out = torch.empty_like(S_in)
+    count = M.numel() // (d * d)
+    st = library().kda_state_compose(_ptr(M), _ptr(S_in), _ptr(S_tilde), _ptr(out), count, d,
+                                     S_in.shape[-1], _stream(dev))
+    _check("kda_state_compose", st)
+    return out
+
+
+def kcp_summaries(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, cu_seqlens: torch.Tensor
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-segment summaries (M, S~) of packed segments, each with two
+    kda_chunk_fwd launches over all segments at once: S~ from S = 0, and M
+    from S = I with v = 0 (d_v = d_k).  Returns ([P, H, d, d], [P, H, d, d_v])."""
+    P = cu_seqlens.shape[0] - 1
+    H, dk = q.shape[-2:]
+    _, S_t = chunk_fwd(q, k, v, g, beta, cu_seqlens=cu_seqlens)
+    eye = torch.eye(dk, dtype=torch.float32, device=q.device).expand(P, H, dk, dk).contiguous()
+    _, M = chunk_fwd(q, k, torch.zeros_like(k), g, beta, initial_state=eye,
+                     cu_seqlens=cu_seqlens)
+    return M, S_t
+
+
+def kcp_scan(M: torch.Tensor, S_tilde: torch.Tensor,
+             S0: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """States entering each segment and the final state: S_in[0] = S0 (or 0),
+    S_in[r + 1] = M[r] S_in[r] + S~[r], one kda_state_compose launch per
+    segment (over all heads)."""
+    P = M.shape[0]
+    S = torch.zeros_like(S_tilde[0]) if S0 is None else S0.contiguous()
+    S_in = torch.empty_like(S_tilde)
+    for r in range(P):
+        S_in[r].copy_(S)
+        S = state_compose(M[r], S, S_tilde[r])
+    return S_in, S

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_layer.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 vector instructions are disabled in every device pass.

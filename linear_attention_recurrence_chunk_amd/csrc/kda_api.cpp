@@ -10,9 +10,21 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, const flo
                           const float *beta, const float *s0, const int32_t *cu, int num_seqs,
                           int64_t seq_len, int H, int d, int chunk, bool is_bf16, void *o,
                           float *sf, hipStream_t stream);
+hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
+                                const void *z, const float *A_log, const float *b_alpha,
+                                const float *beta, const float *s0, const int32_t *cu,
+                                int num_seqs, int64_t seq_len, int H, int d, int chunk,
+                                bool is_bf16, void *o, float *sf, hipStream_t stream);
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, void *o, int64_t NH, int d,
                          bool is_bf16, hipStream_t stream);
+hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *w, float eps,
+                              void *out, int64_t rows, int dv, bool is_bf16, hipStream_t stream);
+hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, int nseq,
+                             int64_t ntok, int C, float *state, void *y, bool is_bf16,
+                             hipStream_t stream);
+hipError_t launch_compose(const float *M, const float *S_in, const float *S_tilde, float *S_out,
+                          int64_t count, int d, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -82,6 +94,80 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
     const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, cu_seqlens,
                                              num_seqs, seq_len, H, d_k, 64,
                                              dtype == KDA_BF16, o, final_state, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void *v, const void *z,
+                               const float *A_log, const float *b_alpha, const float *beta,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
+                               int32_t d_v, int32_t chunk_size, kda_dtype dtype, void *o,
+                               float *final_state, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    // z stands in for g in the common checks (same shape and alignment rule)
+    const kda_status st =
+        prefill_check(q_raw, k_raw, v, reinterpret_cast<const float *>(z), beta, initial_state,
+                      cu_seqlens, num_seqs, total_tokens, H, d_k, d_v, chunk_size, dtype, o,
+                      final_state, workspace, workspace_bytes);
+    if (st != KDA_OK) return st;
+    if (total_tokens > 0 && (!A_log || !b_alpha)) return KDA_ERR_NULL;
+    if (misaligned(A_log) || misaligned(b_alpha)) return KDA_ERR_ALIGN;
+    if (num_seqs == 0) return KDA_OK;
+    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
+    const hipError_t e = kda::launch_prefill_fused(q_raw, k_raw, v, z, A_log, b_alpha, beta,
+                                                   initial_state, cu_seqlens, num_seqs, seq_len,
+                                                   H, d_k, 64, dtype == KDA_BF16, o, final_state,
+                                                   stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_output_gate(const void *o_raw, const void *gate, const float *weight, float eps,
+                           void *out, int64_t rows, int32_t d_v, kda_dtype dtype,
+                           hipStream_t stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (rows < 0 || d_v < 1 || !(eps >= 0.f)) return KDA_ERR_SHAPE;
+    if (d_v != 32 && d_v != 64 && d_v != 128) return KDA_ERR_UNSUPPORTED;
+    if (rows == 0) return KDA_OK;
+    if (!o_raw || !gate || !weight || !out) return KDA_ERR_NULL;
+    if (misaligned(o_raw) || misaligned(gate) || misaligned(weight) || misaligned(out))
+        return KDA_ERR_ALIGN;
+    const hipError_t e =
+        kda::launch_output_gate(o_raw, gate, weight, eps, out, rows, d_v, dtype == KDA_BF16, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_tokens, int32_t channels,
+                          float *conv_state, void *y, kda_dtype dtype, hipStream_t stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || total_tokens < 0 || channels < 1) return KDA_ERR_SHAPE;
+    if (channels % 4 != 0) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_SHAPE;
+    if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_SHAPE;
+    if (num_seqs == 0) return KDA_OK;
+    if (!weight || (total_tokens > 0 && (!x || !y))) return KDA_ERR_NULL;
+    if (misaligned(x) || misaligned(weight) || misaligned(cu_seqlens) || misaligned(conv_state) ||
+        misaligned(y))
+        return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_short_conv(x, weight, cu_seqlens, num_seqs, total_tokens,
+                                                channels, conv_state, y, dtype == KDA_BF16, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_state_compose(const float *M, const float *S_in, const float *S_tilde,
+                             float *S_out, int64_t count, int32_t d_k, int32_t d_v,
+                             hipStream_t stream)
+{
+    if (count < 0 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
+    if (d_k != d_v || (d_k != 32 && d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+    if (count == 0) return KDA_OK;
+    if (!M || !S_in || !S_tilde || !S_out) return KDA_ERR_NULL;
+    if (misaligned(M) || misaligned(S_in) || misaligned(S_tilde) || misaligned(S_out))
+        return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_compose(M, S_in, S_tilde, S_out, count, d_k, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -100,6 +100,8 @@ struct Smem {
     float eE[Cf::NB + 1][DK];   // prod_{m<J} e^{B_m}; row NB: whole-chunk decay
     float eTi[Cf::NB][DK];      // prod_{m>=J} e^{B_m}
     float beta[Cf::C];
+    float nrm[2][Cf::C][Cf::WPB];  // fused prologue: partial sums of squares of k, q rows
+    float bA[DK];                  // fused prologue: decay bias b_alpha^h of the head
 };
 
 // two and four elements; `eight_bytes` is the 8-byte vector of the value loads
@@ -114,6 +116,7 @@ template <typename T, int DK, int BV>
 struct ChunkRegs {
     typedef Cfg<T, DK, BV> Cf;
     f32x2 g[4];
+    typename Vec<T>::two z[4];          // fused prologue: decay logits instead of g
     typename Vec<T>::two k[4], q[4];
     typename Vec<T>::eight_bytes v[Cf::NVV];
     float beta;
@@ -140,11 +143,11 @@ __device__ __forceinline__ uint32_t row_off(int row, int64_t nvalid, int rowstri
 // the next chunk's loads can be spread over the phases of the current one.
 enum { LOAD_G = 1, LOAD_KQ = 2, LOAD_VB = 4, LOAD_ALL = 7 };
 
-template <typename T, int DK, int BV>
+template <bool FUSED, typename T, int DK, int BV>
 __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, const SeqView &sv,
                                            int64_t t0, const T *__restrict__ q,
                                            const T *__restrict__ k, const T *__restrict__ v,
-                                           const float *__restrict__ g,
+                                           const float *__restrict__ g, const T *__restrict__ z,
                                            const float *__restrict__ beta, int DV)
 {
     typedef Cfg<T, DK, BV> Cf;
@@ -159,7 +162,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t off = row_off(16 * I + 4 * qr + r, nvalid, rs) + 2 * cp;
-            if (parts & LOAD_G) R.g[r] = *reinterpret_cast<const f32x2 *>(g + cbase + off);
+            if (parts & LOAD_G) {
+                if (FUSED) R.z[r] = *reinterpret_cast<const V2 *>(z + cbase + off);
+                else R.g[r] = *reinterpret_cast<const f32x2 *>(g + cbase + off);
+            }
             if (parts & LOAD_KQ) {
                 R.k[r] = *reinterpret_cast<const V2 *>(k + cbase + off);
                 R.q[r] = *reinterpret_cast<const V2 *>(q + cbase + off);
@@ -228,14 +234,34 @@ template <typename T> __device__ __forceinline__ void unpack4(typename Vec<T>::f
 }
 
 
+// Per-workgroup constant of the fused prologue: e^{A_h} (the decay bias is in
+// LDS).
+struct GateCtx {
+    float eA;
+};
+
+// g = g_min sigma(e^{A_h} (z + b_alpha^h)) ("Glossaire", entry "Decroissance
+// bornee", with the per-head bias of the notation table), returned as
+// alpha = e^g.
+__device__ __forceinline__ float bounded_alpha(float z, float eA, float b)
+{
+    constexpr float kGMin = -5.f;
+    const float x = eA * (z + b);
+    const float s = __builtin_amdgcn_rcpf(1.f + __expf(-x));
+    return __expf(kGMin * s);
+}
+
 // Elementwise phase for one chunk: from the raw g, k, q of this thread's item
 // (sub-block I, channels 2 cp and 2 cp + 1, rows 4 qr .. 4 qr + 3 of the
 // sub-block), the sub-block-local decays and the operand tiles K o e^L,
 // Q o e^L, K o e^{B-L}, K o e^-L and e^{B_I}; then
 // this thread's share of beta and of the value slice.  FULL: every row of the
-// chunk lies in the sequence.
-template <bool FULL, typename T, int DK, int BV>
-__device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv)
+// chunk lies in the sequence.  FUSED: g comes from decay logits through the
+// bounded gate, and k and q are divided by their row norms (L2Norm of the
+// function table), whose partial sums of squares are in sm.nrm.
+template <bool FULL, bool FUSED, typename T, int DK, int BV>
+__device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
+                                        const GateCtx &gc)
 {
     typedef Cfg<T, DK, BV> Cf;
     typedef typename Vec<T>::two V2;
@@ -245,13 +271,23 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
         const int lp = opaque_lane(), n16 = lp & 15, qr = lp >> 4;
         const int I = wv / Cf::WPB, cp = (wv % Cf::WPB) * 16 + n16;
         const int r0 = 16 * I + 4 * qr;
+        float bb[2] = {0.f, 0.f};
+        if (FUSED) {
+            const f32x2 b2 = *reinterpret_cast<const f32x2 *>(&sm.bA[2 * cp]);
+            bb[0] = b2[0];
+            bb[1] = b2[1];
+        }
         // per channel: e^{L_r} (eL) and e^{B - L_r} (sx) for the four rows, e^{-B}
         float eL[2][4], sx[2][4], rb[2], ebv[2];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             float a[4], pl[4], sl[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = (FULL || r0 + r < nv) ? __expf(R.g[r][cc]) : 1.f;
+            for (int r = 0; r < 4; ++r) {
+                const float ar = FUSED ? bounded_alpha(to_f32(R.z[r][cc]), gc.eA, bb[cc])
+                                       : __expf(R.g[r][cc]);
+                a[r] = (FULL || r0 + r < nv) ? ar : 1.f;
+            }
             pl[0] = a[0];
 #pragma unroll
             for (int r = 1; r < 4; ++r) pl[r] = pl[r - 1] * a[r];
@@ -275,11 +311,27 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const bool in = FULL || r0 + r < nv;
+            // fused prologue: 1 / ||k_r||, 1 / ||q_r|| (0 for a zero row)
+            float ik = 1.f, iq = 1.f;
+            if (FUSED) {
+                float s2k = 0.f, s2q = 0.f;
+#pragma unroll
+                for (int w = 0; w < Cf::WPB; ++w) {
+                    s2k += sm.nrm[0][r0 + r][w];
+                    s2q += sm.nrm[1][r0 + r][w];
+                }
+                ik = s2k > 0.f ? __builtin_amdgcn_rsqf(s2k) : 0.f;
+                iq = s2q > 0.f ? __builtin_amdgcn_rsqf(s2q) : 0.f;
+            }
             float kk[2], qq[2], kc[2], kd[2];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 kk[cc] = in ? to_f32(R.k[r][cc]) : 0.f;
                 qq[cc] = in ? to_f32(R.q[r][cc]) : 0.f;
+                if (FUSED) {
+                    kk[cc] *= ik;
+                    qq[cc] *= iq;
+                }
                 kc[cc] = kk[cc] * sx[cc][r];              // e^{B - L_r} <= 1
                 kd[cc] = kc[cc] * rb[cc];                 // e^{-L_r} <= e^80
             }
@@ -302,11 +354,49 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
     }
 }
 
-template <typename T, int DK, int BV>
-__device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv)
+template <bool FUSED, typename T, int DK, int BV>
+__device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
+                                        const GateCtx &gc)
 {
-    if (nv >= Cfg<T, DK, BV>::C) e_phase<true>(sm, R, nv);
-    else e_phase<false>(sm, R, nv);
+    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED>(sm, R, nv, gc);
+    else e_phase<false, FUSED>(sm, R, nv, gc);
+}
+
+// Sum over the 16 lanes of a row of the wave (lanes 16 j .. 16 j + 15), with
+// DPP moves: swap neighbours, swap pairs, then rotate the row by 4 and by 8.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    return x;
+}
+
+// Fused prologue: partial sums of squares of the raw k and q rows of this
+// thread's item, over the wave's 32 channels; lane 0 of each row quarter
+// stores them for the elementwise phase, which adds the WPB partials of a row.
+template <typename T, int DK, int BV>
+__device__ __forceinline__ void norm_partials(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R)
+{
+    typedef Cfg<T, DK, BV> Cf;
+    const int wv = wave_id();
+    if (wv < Cf::EWAVES) {
+        const int lp = opaque_lane(), n16 = lp & 15, qr = lp >> 4;
+        const int I = wv / Cf::WPB, part = wv % Cf::WPB;
+        const int r0 = 16 * I + 4 * qr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float k0 = to_f32(R.k[r][0]), k1 = to_f32(R.k[r][1]);
+            const float q0 = to_f32(R.q[r][0]), q1 = to_f32(R.q[r][1]);
+            const float sk = row16_sum(k0 * k0 + k1 * k1);
+            const float sq = row16_sum(q0 * q0 + q1 * q1);
+            if (n16 == 0) {
+                sm.nrm[0][r0 + r][part] = sk;
+                sm.nrm[1][r0 + r][part] = sq;
+            }
+        }
+    }
 }
 
 // Off-diagonal blocks (I, J < I) of A (stored negated, beta applied) and of P.
@@ -391,12 +481,15 @@ __device__ __forceinline__ int rows_in(int64_t t0, int64_t eos, int C)
     return n < C ? (int)n : C;
 }
 
-template <typename T, int DK, int BV, int DV>
+// FUSED: q and k arrive unnormalised and g is replaced by decay logits z with
+// the per-head gate parameters A_log [H] and b_alpha [H][DK].
+template <typename T, int DK, int BV, int DV, bool FUSED>
 __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ s0, const int32_t *__restrict__ cu_seqlens, int num_seqs,
-    int64_t seq_len, int H, T *__restrict__ o, float *__restrict__ sfinal)
+    int64_t seq_len, int H, T *__restrict__ o, float *__restrict__ sfinal,
+    const T *__restrict__ z, const float *__restrict__ A_log, const float *__restrict__ b_alpha)
 {
     typedef Cfg<T, DK, BV> Cf;
     typedef Path<T> PT;
@@ -463,11 +556,24 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const bool has_job = wv < Cf::NJOB;
     const int jI = wv / NVT, jvt = wv % NVT;
 
+    GateCtx gc;
+    gc.eA = 1.f;
+    if (FUSED) {
+        gc.eA = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                              __builtin_bit_cast(int, __expf(A_log[head]))));
+        for (int c = t; c < DK; c += NT) sm.bA[c] = b_alpha[(int64_t)head * DK + c];
+        __syncthreads();
+    }
+
     const int64_t nchunks = (sv.eos - sv.bos + C - 1) / C;
     ChunkRegs<T, DK, BV> R;
     if (nchunks > 0) {
-        load_chunk(R, LOAD_ALL, sv, sv.bos, q, k, v, g, beta, DV);
-        e_phase(sm, R, rows_in(sv.bos, sv.eos, C));
+        load_chunk<FUSED>(R, LOAD_ALL, sv, sv.bos, q, k, v, g, z, beta, DV);
+        if (FUSED) {
+            norm_partials(sm, R);
+            __syncthreads();
+        }
+        e_phase<FUSED>(sm, R, rows_in(sv.bos, sv.eos, C), gc);
     }
     __syncthreads();
 
@@ -477,7 +583,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         const int64_t t0 = sv.bos + ch * C;
         const int nv = rows_in(t0, sv.eos, C);           // rows of this chunk in the sequence
         const bool more = ch + 1 < nchunks;
-        if (more) load_chunk(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, beta, DV);
+        if (more) load_chunk<FUSED>(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, z, beta, DV);
 
         // ================= AP
         if (wv < NB) {
@@ -581,7 +687,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             }
         }
         __syncthreads();   // ---------------------------------------------- B1
-        if (more) load_chunk(R, LOAD_VB, sv, t0 + C, q, k, v, g, beta, DV);
+        if (more) load_chunk<FUSED>(R, LOAD_VB, sv, t0 + C, q, k, v, g, z, beta, DV);
 
         // ================= YZ: state read-out and R = B (V - Y), stored transposed
         f32x4 Zt = zero4();
@@ -597,6 +703,8 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 rv[i] = b4[i] * (to_f32(sm.V[16 * jI + 4 * grp + i][16 * jvt + n16]) - Y[i]);
             *reinterpret_cast<V4 *>(&sm.RT[16 * jvt + n16][16 * jI + 4 * grp]) = pack4<T>(rv);
         }
+        // fused prologue: the next chunk's row norms, read by its E after B2
+        if (FUSED && more) norm_partials(sm, R);
         __syncthreads();   // ---------------------------------------------- B2
 
         // ================= U: forward substitution, one wave per value tile;
@@ -625,7 +733,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         }
         // ================= the next chunk's elementwise phase (the substituting
         // waves do their share after their substitution)
-        if (more) e_phase(sm, R, rows_in(t0 + C, sv.eos, C));
+        if (more) e_phase<FUSED>(sm, R, rows_in(t0 + C, sv.eos, C), gc);
         __syncthreads();   // ---------------------------------------------- B3
 
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
@@ -696,18 +804,44 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     }
 }
 
-template <typename T, int D, int BV>
+template <typename T, int D, int BV, bool FUSED>
 static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *s0, const int32_t *cu,
                                    int num_seqs, int64_t seq_len, int H, void *o, float *sf,
+                                   const void *z, const float *A_log, const float *b_alpha,
                                    hipStream_t stream)
 {
     const int64_t nwork = (int64_t)num_seqs * H * (D / BV);
     if (nwork == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D>), dim3((unsigned)nwork),
+    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FUSED>), dim3((unsigned)nwork),
                        dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)q, (const T *)k,
-                       (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (T *)o, sf);
+                       (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (T *)o, sf,
+                       (const T *)z, A_log, b_alpha);
     return hipGetLastError();
+}
+
+template <bool FUSED>
+static hipError_t launch_prefill_f(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const float *s0, const int32_t *cu,
+                                   int num_seqs, int64_t seq_len, int H, int d, bool is_bf16,
+                                   void *o, float *sf, const void *z, const float *A_log,
+                                   const float *b_alpha, hipStream_t stream)
+{
+#define KDA_PREFILL_ARGS q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, o, sf, z, A_log, b_alpha, stream
+    if (is_bf16) {
+        switch (d) {
+            case 32: return launch_prefill_t<bf16, 32, 32, FUSED>(KDA_PREFILL_ARGS);
+            case 64: return launch_prefill_t<bf16, 64, 64, FUSED>(KDA_PREFILL_ARGS);
+            case 128: return launch_prefill_t<bf16, 128, 64, FUSED>(KDA_PREFILL_ARGS);
+        }
+    } else {
+        switch (d) {
+            case 32: return launch_prefill_t<float, 32, 32, FUSED>(KDA_PREFILL_ARGS);
+            case 64: return launch_prefill_t<float, 64, 32, FUSED>(KDA_PREFILL_ARGS);
+        }
+    }
+#undef KDA_PREFILL_ARGS
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -716,29 +850,19 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, const flo
                           float *sf, hipStream_t stream)
 {
     if (chunk != 64) return hipErrorInvalidValue;
-    if (is_bf16) {
-        switch (d) {
-            case 32:
-                return launch_prefill_t<bf16, 32, 32>(q, k, v, g, beta, s0, cu, num_seqs,
-                                                      seq_len, H, o, sf, stream);
-            case 64:
-                return launch_prefill_t<bf16, 64, 64>(q, k, v, g, beta, s0, cu, num_seqs,
-                                                      seq_len, H, o, sf, stream);
-            case 128:
-                return launch_prefill_t<bf16, 128, 64>(q, k, v, g, beta, s0, cu, num_seqs,
-                                                       seq_len, H, o, sf, stream);
-        }
-    } else {
-        switch (d) {
-            case 32:
-                return launch_prefill_t<float, 32, 32>(q, k, v, g, beta, s0, cu, num_seqs,
-                                                       seq_len, H, o, sf, stream);
-            case 64:
-                return launch_prefill_t<float, 64, 32>(q, k, v, g, beta, s0, cu, num_seqs,
-                                                       seq_len, H, o, sf, stream);
-        }
-    }
-    return hipErrorInvalidValue;
+    return launch_prefill_f<false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d, is_bf16, o,
+                                   sf, nullptr, nullptr, nullptr, stream);
+}
+
+hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
+                                const void *z, const float *A_log, const float *b_alpha,
+                                const float *beta, const float *s0, const int32_t *cu,
+                                int num_seqs, int64_t seq_len, int H, int d, int chunk,
+                                bool is_bf16, void *o, float *sf, hipStream_t stream)
+{
+    if (chunk != 64) return hipErrorInvalidValue;
+    return launch_prefill_f<true>(q_raw, k_raw, v, nullptr, beta, s0, cu, num_seqs, seq_len, H, d,
+                                  is_bf16, o, sf, z, A_log, b_alpha, stream);
 }
 
 }  // namespace kda

@@ -72,6 +72,11 @@ WORKLOADS: Dict[str, Workload] = {
     # One decode step for 256 requests with fp32 states ~ N(0, 0.02).
     "k3_decode_256": Workload("k3_decode_256", H=96, dk=128, dv=128, decode_requests=256,
                               state_std=0.02),
+    # nano-K3 (the toy model of the pages: 8 heads x 64, context 2048): a batch
+    # of 32 full-context sequences, and one decode step for 256 requests.
+    "nano_k3_prefill": Workload("nano_k3_prefill", H=8, dk=64, dv=64, chunk=64, B=32, T=2048),
+    "nano_k3_decode": Workload("nano_k3_decode", H=8, dk=64, dv=64, decode_requests=256,
+                               state_std=0.02),
 }
 
 
@@ -151,3 +156,25 @@ def decode_inputs(w: Workload, seed: int, device="cpu", requests: Optional[int] 
 def custom(name="custom", **kw) -> Workload:
     """A workload with explicit fields (tests use it for edge shapes)."""
     return Workload(name=name, **kw)
+
+
+def layer_inputs(w: Workload, seed: int, device="cuda") -> Dict[str, torch.Tensor]:
+    """Raw inputs of the layer steps for a prefill workload (no normalisation,
+    no gate applied): q_raw, k_raw ~ N(0, 1) and decay logits z ~ N(gate_mu,
+    gate_sigma) in the workload dtype; A_log = 0 and b_alpha = 0 (so that the
+    bounded gate reproduces the workload's g distribution); output-gate logits
+    ~ N(0, 1); RMSNorm weight ~ N(1, 0.1); ShortConv taps ~ N(0, 0.5) over the
+    H * d_k channels of one projection."""
+    gen = _gen(seed, device)
+    n = sum(sequence_lengths(w, seed))
+    r = lambda *s: torch.randn(*s, generator=gen, device=device)
+    return {
+        "q_raw": r(n, w.H, w.dk).to(w.dtype),
+        "k_raw": r(n, w.H, w.dk).to(w.dtype),
+        "z": (w.gate_mu + w.gate_sigma * r(n, w.H, w.dk)).to(w.dtype),
+        "A_log": torch.zeros(w.H, device=device),
+        "b_alpha": torch.zeros(w.H, w.dk, device=device),
+        "gate": r(n, w.H, w.dv).to(w.dtype),
+        "rms_weight": 1.0 + 0.1 * r(w.dv),
+        "conv_w": 0.5 * r(w.H * w.dk, 4),
+    }

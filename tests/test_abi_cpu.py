@@ -29,7 +29,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = _lib.library()
     names = _declared_functions()
     assert names == sorted(["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_step_decode",
-                            "kda_status_string", "kda_version"])
+                            "kda_status_string", "kda_version", "kda_chunk_fwd_fused",
+                            "kda_output_gate", "kda_short_conv", "kda_state_compose"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -123,3 +124,49 @@ def test_python_binding_validates_before_the_call():
         _lib.chunk_fwd(q, q, q, q, torch.zeros(8, 3))
     with pytest.raises(ValueError):
         _lib.step_decode(q, q, q, q, torch.zeros(8, 2), torch.zeros(8, 2, 32, 16))
+
+
+def _fused(**kw):
+    a = dict(q=A, k=A, v=A, z=A, Al=A, b=A, beta=A, s0=None, cu=None, num_seqs=1, total=128, H=2,
+             dk=64, dv=64, chunk=64, dt=1, o=A, sf=None)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _lib.library().kda_chunk_fwd_fused(
+        p(a["q"]), p(a["k"]), p(a["v"]), p(a["z"]), p(a["Al"]), p(a["b"]), p(a["beta"]),
+        p(a["s0"]), p(a["cu"]), a["num_seqs"], a["total"], a["H"], a["dk"], a["dv"], a["chunk"],
+        a["dt"], p(a["o"]), p(a["sf"]), None, 0, None)
+
+
+@gpu_visible
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), ENULL), (dict(Al=None), ENULL), (dict(b=None), ENULL), (dict(q=None), ENULL),
+    (dict(dk=48, dv=48), EUNSUP), (dict(chunk=32), EUNSUP), (dict(num_seqs=3), ESHAPE),
+    (dict(z=MIS), EALIGN), (dict(Al=MIS), EALIGN), (dict(b=MIS), EALIGN),
+])
+def test_chunk_fwd_fused_rejects(kw, status):
+    assert _fused(**kw) == status
+
+
+@gpu_visible
+def test_layer_steps_reject():
+    lib = _lib.library()
+    p = ctypes.c_void_p
+    # output gate: rows, d_v, dtype, pointers, alignment
+    assert lib.kda_output_gate(p(A), p(A), p(A), 1e-5, p(A), -1, 128, 1, None) == ESHAPE
+    assert lib.kda_output_gate(p(A), p(A), p(A), 1e-5, p(A), 10, 96, 1, None) == EUNSUP
+    assert lib.kda_output_gate(p(A), p(A), p(A), -1.0, p(A), 10, 128, 1, None) == ESHAPE
+    assert lib.kda_output_gate(p(A), None, p(A), 1e-5, p(A), 10, 128, 1, None) == ENULL
+    assert lib.kda_output_gate(p(A), p(A), p(MIS), 1e-5, p(A), 10, 128, 1, None) == EALIGN
+    assert lib.kda_output_gate(None, None, None, 1e-5, None, 0, 128, 1, None) == OK
+    # short conv: channels multiple of 4, sequence layout, pointers
+    assert lib.kda_short_conv(p(A), p(A), None, 2, 10, 6, None, p(A), 1, None) == EUNSUP
+    assert lib.kda_short_conv(p(A), p(A), None, 3, 10, 8, None, p(A), 1, None) == ESHAPE
+    assert lib.kda_short_conv(p(A), None, None, 2, 10, 8, None, p(A), 1, None) == ENULL
+    assert lib.kda_short_conv(p(A), p(A), None, 2, 10, 8, p(MIS), p(A), 1, None) == EALIGN
+    assert lib.kda_short_conv(p(A), p(A), None, 0, 0, 8, None, p(A), 1, None) == OK
+    # state compose: square states of a supported size
+    assert lib.kda_state_compose(p(A), p(A), p(A), p(A), 4, 64, 32, None) == EUNSUP
+    assert lib.kda_state_compose(p(A), p(A), p(A), p(A), -1, 64, 64, None) == ESHAPE
+    assert lib.kda_state_compose(p(A), None, p(A), p(A), 4, 64, 64, None) == ENULL
+    assert lib.kda_state_compose(p(A), p(A), p(A), p(MIS), 4, 64, 64, None) == EALIGN
+    assert lib.kda_state_compose(None, None, None, None, 0, 64, 64, None) == OK

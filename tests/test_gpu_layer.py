@@ -1,0 +1,202 @@
+"""GPU parity of the layer steps around the recurrence (fused front end, output
+gate, ShortConv, segment composition) against the fp64 oracle, through the C
+ABI.  The oracle reads the same (bf16-rounded) tensors the GPU receives."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import layer_ref as L
+import linear_attention_recurrence_chunk_amd as kda
+
+pytestmark = pytest.mark.gpu
+dev = "cuda"
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+def _np(x):
+    return x.detach().to("cpu", torch.float64).numpy()
+
+
+def _fused_inputs(lens, H, d, dtype, seed, state_std=0.0):
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    n = sum(lens)
+    r = lambda *s: torch.randn(*s, generator=gen, device=dev)
+    q_raw = (2.0 * r(n, H, d)).to(dtype)
+    k_raw = (0.5 * r(n, H, d)).to(dtype)
+    v = r(n, H, d).to(dtype)
+    z = (r(n, H, d) + 1.0).to(dtype)
+    A_log = 0.3 * r(H)
+    b_alpha = 0.5 * r(H, d)
+    beta = torch.sigmoid(r(n, H))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    s0 = state_std * r(len(lens), H, d, d) if state_std else None
+    return q_raw, k_raw, v, z, A_log, b_alpha, beta, cu, s0
+
+
+def _fused_oracle(q_raw, k_raw, v, z, A_log, b_alpha, beta, cu, s0, heads=None):
+    sel = (slice(None), slice(None) if heads is None else heads)
+    q = L.l2norm(_np(q_raw)[sel])
+    k = L.l2norm(_np(k_raw)[sel])
+    hsel = slice(None) if heads is None else heads
+    g = L.bounded_gate(_np(z)[sel], _np(A_log)[hsel], _np(b_alpha)[hsel])
+    s0n = None if s0 is None else _np(s0)[:, hsel]
+    return oracle.forward(q, k, _np(v)[sel], g, _np(beta)[sel], initial_state=s0n,
+                          cu_seqlens=cu.cpu().numpy().astype(np.int64))
+
+
+@pytest.mark.parametrize("dtype,d,lens,state_std,tol", [
+    (torch.bfloat16, 128, [300], 0.0, 2e-2),
+    (torch.bfloat16, 128, [64, 1, 0, 129, 200], 0.05, 2e-2),
+    (torch.bfloat16, 64, [250, 63], 0.05, 2e-2),
+    (torch.bfloat16, 32, [333], 0.0, 2e-2),
+    (torch.float32, 32, [100, 0, 77, 256], 0.1, 1e-4),
+    (torch.float32, 64, [190], 0.1, 1e-4),
+])
+def test_fused_prologue_prefill(dtype, d, lens, state_std, tol):
+    H = 3
+    args = _fused_inputs(lens, H, d, dtype, seed=d + len(lens), state_std=state_std)
+    q_raw, k_raw, v, z, A_log, b_alpha, beta, cu, s0 = args
+    o, sf = kda.chunk_fwd_fused(q_raw, k_raw, v, z, A_log, b_alpha, beta, initial_state=s0,
+                                cu_seqlens=cu)
+    torch.cuda.synchronize()
+    o_ref, s_ref = _fused_oracle(*args)
+    eo, es = _rel(_np(o), o_ref), _rel(_np(sf), s_ref)
+    print(f"[parity] fused prologue {dtype} d={d} lens={lens}: o={eo:.3e}, state={es:.3e}")
+    assert eo <= tol and es <= tol
+
+
+def test_fused_prologue_k3_8k_sampled_heads():
+    H, d, T = 96, 128, 8192
+    args = _fused_inputs([T], H, d, torch.bfloat16, seed=7)
+    q_raw, k_raw, v, z, A_log, b_alpha, beta, cu, s0 = args
+    o, sf = kda.chunk_fwd_fused(q_raw, k_raw, v, z, A_log, b_alpha, beta, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    heads = [0, 95]
+    o_ref, s_ref = _fused_oracle(*args, heads=heads)
+    eo, es = _rel(_np(o)[:, heads], o_ref), _rel(_np(sf)[:, heads], s_ref)
+    print(f"[parity] fused prologue 8k x 96 heads {heads}: o={eo:.3e}, state={es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_fused_prologue_zero_rows_stay_zero():
+    # a zero key row is left at zero (no NaN from 0/0); it then writes nothing
+    H, d = 2, 64
+    args = list(_fused_inputs([130], H, d, torch.bfloat16, seed=11))
+    args[1][5:9] = 0
+    args[0][70] = 0
+    o, sf = kda.chunk_fwd_fused(*args[:7], cu_seqlens=args[7])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(sf).all()
+    o_ref, s_ref = _fused_oracle(*args)
+    assert _rel(_np(o), o_ref) <= 2e-2 and _rel(_np(sf), s_ref) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,d,tol", [(torch.bfloat16, 128, 1e-2), (torch.bfloat16, 64, 1e-2),
+                                         (torch.float32, 128, 1e-5), (torch.float32, 32, 1e-5)])
+def test_output_gate(dtype, d, tol):
+    gen = torch.Generator(device=dev).manual_seed(d)
+    rows = 3 * 1000 + 7
+    o_raw = (3.0 * torch.randn(rows, d, generator=gen, device=dev)).to(dtype)
+    gate = (2.0 * torch.randn(rows, d, generator=gen, device=dev)).to(dtype)
+    w = torch.randn(d, generator=gen, device=dev)
+    out = kda.output_gate(o_raw, gate, w)
+    ref = L.output_gate(_np(o_raw), _np(gate), _np(w))
+    torch.cuda.synchronize()
+    e = _rel(_np(out), ref)
+    print(f"[parity] output gate {dtype} d={d}: {e:.3e}")
+    assert e <= tol
+    # in place: out aliases o_raw
+    again = kda.output_gate(o_raw, gate, w, out=o_raw)
+    torch.cuda.synchronize()
+    assert again.data_ptr() == o_raw.data_ptr() and _rel(_np(o_raw), ref) <= tol
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_short_conv_prefill(dtype, with_state):
+    gen = torch.Generator(device=dev).manual_seed(3)
+    lens = [5, 0, 1, 2, 300, 64]
+    C = 96
+    n = sum(lens)
+    x = torch.randn(n, C, generator=gen, device=dev).to(dtype)
+    w = torch.randn(C, 4, generator=gen, device=dev)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    st = torch.randn(len(lens), 3, C, generator=gen, device=dev) if with_state else None
+    st_in = None if st is None else _np(st)
+    y = kda.short_conv(x, w, cu_seqlens=cu, conv_state=st)
+    torch.cuda.synchronize()
+    y_ref, st_ref = L.short_conv(_np(x), _np(w), cu_seqlens=cu.cpu().numpy(), conv_state=st_in)
+    e = _rel(_np(y), y_ref)
+    print(f"[parity] short conv {dtype} state={with_state}: {e:.3e}")
+    assert e <= (1e-2 if dtype == torch.bfloat16 else 1e-6)
+    if with_state:
+        np.testing.assert_array_equal(_np(st), st_ref)    # copies of inputs: exact
+
+
+def test_short_conv_decode_steps_equal_prefill():
+    gen = torch.Generator(device=dev).manual_seed(4)
+    N, T, C = 8, 6, 64
+    x = torch.randn(N, T, C, generator=gen, device=dev).to(torch.bfloat16)
+    w = torch.randn(C, 4, generator=gen, device=dev)
+    st0 = torch.randn(N, 3, C, generator=gen, device=dev)
+    st = st0.clone()
+    ys = [kda.short_conv(x[:, t].contiguous(), w, conv_state=st, num_seqs=N) for t in range(T)]
+    st_p = st0.clone()
+    yp = kda.short_conv(x.reshape(N * T, C), w, conv_state=st_p, num_seqs=N)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(ys, 1).reshape(N * T, C), yp)
+    assert torch.equal(st, st_p)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_state_compose(d):
+    gen = torch.Generator(device=dev).manual_seed(d)
+    cnt = 37
+    M = torch.randn(cnt, d, d, generator=gen, device=dev) / np.sqrt(d)
+    S = torch.randn(cnt, d, d, generator=gen, device=dev)
+    St = torch.randn(cnt, d, d, generator=gen, device=dev)
+    out = kda.state_compose(M, S, St)
+    torch.cuda.synchronize()
+    ref = _np(M) @ _np(S) + _np(St)
+    e = _rel(_np(out), ref)
+    print(f"[parity] state compose d={d}: {e:.3e}")
+    assert e <= 1e-5
+
+
+def test_kcp_segments_compose_to_the_whole_sequence():
+    H, d = 4, 128
+    cuts = [0, 500, 501, 621, 2048]
+    T = cuts[-1]
+    gen = torch.Generator(device=dev).manual_seed(21)
+    r = lambda *s: torch.randn(*s, generator=gen, device=dev)
+    q = torch.nn.functional.normalize(r(T, H, d), dim=-1).to(torch.bfloat16)
+    k = torch.nn.functional.normalize(r(T, H, d), dim=-1).to(torch.bfloat16)
+    v = r(T, H, d).to(torch.bfloat16)
+    # weak decays (long memory), so that a 120-token transition product stays
+    # far above the float range's floor and the check of M means something
+    g = -5.0 * torch.sigmoid(r(T, H, d) - 6.0)
+    beta = torch.sigmoid(r(T, H))
+    S0 = 0.05 * r(1, H, d, d)
+    cu = torch.tensor(cuts, dtype=torch.int32, device=dev)
+    M, St = kda.kcp_summaries(q, k, v, g, beta, cu)
+    S_in, S_end = kda.kcp_scan(M, St, S0[0])
+    torch.cuda.synchronize()
+    qn, kn, vn, gn, bn = (_np(x) for x in (q, k, v, g, beta))
+    _, s_ref = oracle.forward(qn, kn, vn, gn, bn, initial_state=_np(S0))
+    e_end = _rel(_np(S_end), s_ref[0])
+    # the transition of one segment against the oracle's product of transitions
+    a, b = cuts[2], cuts[3]
+    m_ref = np.stack([L.transition_product(kn[a:b, h], gn[a:b, h], bn[a:b, h]) for h in range(H)])
+    assert np.max(np.abs(m_ref)) > 1e-3
+    e_m = _rel(_np(M[2]), m_ref)
+    # the state entering the third segment against the oracle's prefix
+    _, s_pref = oracle.forward(qn[:a], kn[:a], vn[:a], gn[:a], bn[:a], initial_state=_np(S0))
+    e_in = _rel(_np(S_in[2]), s_pref[0])
+    print(f"[parity] KCP: final={e_end:.3e}, M={e_m:.3e}, entering={e_in:.3e}")
+    assert e_end <= 2e-2 and e_m <= 2e-2 and e_in <= 2e-2
