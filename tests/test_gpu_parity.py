@@ -124,6 +124,27 @@ def test_prefill_k3_8k():
     assert eo <= 2e-2 and es <= 2e-2
 
 
+def test_prefill_nano_k3_full_size():
+    # the second workload: 32 sequences x 2048 tokens, 8 heads of 64, every head
+    w = inputs.WORKLOADS["nano_k3_prefill"]
+    x = inputs.prefill_inputs(w, seed=2, device=DEV)
+    eo, es = run_prefill(x, w.chunk)
+    report("prefill nano-K3 32 x 2048 x 8 x 64", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_decode_nano_k3():
+    w = inputs.WORKLOADS["nano_k3_decode"]
+    x = inputs.decode_inputs(w, seed=5, device=DEV)
+    st0 = x["state"].cpu()
+    o = kda.step_decode(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"])
+    torch.cuda.synchronize()
+    o_ref, st_ref = oracle.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], st0)
+    eo, es = rel_err(o, o_ref), rel_err(x["state"], st_ref)
+    report("decode nano-K3 N=256", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
+
+
 def test_prefill_chunk_128_equals_chunk_64_and_oracle():
     w = inputs.custom(H=3, dk=128, dv=128, seqlens=[300, 129], state_std=0.05)
     x = inputs.prefill_inputs(w, seed=17, device=DEV)
