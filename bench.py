@@ -62,6 +62,38 @@ def _gbs(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def bench_configs(args, torch, kda, inputs, dev):
+    """The other workloads of the benchmark table, each timed on its own: the
+    tiny fp32 case, the 131072-token sequence (chunk_size 128) and the 16
+    packed sequences with prefix states."""
+    res = {}
+    for name, steps in (("tiny_fp32", args.steps), ("k3_prefill_128k", 5), ("k3_varlen_prefix", 5)):
+        wc = inputs.WORKLOADS[name]
+        xc = inputs.prefill_inputs(wc, seed=2, device=dev)
+        nt, ns = int(xc["q"].shape[0]), len(xc["seqlens"])
+        oc = torch.empty_like(xc["v"])
+        sfc = torch.empty((ns, wc.H, wc.dk, wc.dv), dtype=torch.float32, device=dev)
+
+        def cstep():
+            kda.chunk_fwd(xc["q"], xc["k"], xc["v"], xc["g"], xc["beta"], xc["initial_state"],
+                          xc["cu_seqlens"], chunk_size=wc.chunk, out=oc, final_state=sfc)
+
+        ms, _ = time_launches(cstep, steps, 2, torch)
+        e = xc["q"].element_size()
+        b = prefill_bytes(nt, ns, wc.H, wc.dk, wc.dv, e, e, xc["initial_state"] is not None, True)
+        f = prefill_flops(nt, wc.H, wc.dk, wc.dv, EXEC_CHUNK)
+        res[name] = {"tokens": nt, "sequences": ns, "H": wc.H, "d": wc.dk, "chunk": wc.chunk,
+                     "ms_per_step": ms, "tokens/s": nt / (ms * 1e-3),
+                     "roofline": {"bound": "hbm", "achieved": _gbs(b, ms), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": _gbs(b, ms) / HBM_PEAK_GBS,
+                                  "traffic": None, "kernel": "kda::prefill_kernel",
+                                  "bytes_per_launch": b},
+                     "mfma_frac": f / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        del xc, oc, sfc
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_layer(args, w, x, torch, kda, inputs, dev):
     """The layer steps around the recurrence, each on the prefill workload's
     shapes, plus the nano-K3 prefill and decode: one JSON object."""
@@ -238,6 +270,8 @@ def main():
     ap.add_argument("--decode-workload", default="k3_decode_256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (tiny fp32, 128K tokens, varlen with prefixes)")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the layer steps (fused front end, output gate, ShortConv, "
                          "segment composition) and the nano-K3 shapes")
@@ -325,6 +359,8 @@ def main():
 
     if not args.no_layer:
         out["layer"] = bench_layer(args, w, x, torch, kda, inputs, dev)
+    if not args.no_configs:
+        out["other_configs"] = bench_configs(args, torch, kda, inputs, dev)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()
