@@ -39,12 +39,15 @@
 //        in the previous chunk's U phase.
 //   AP   waves 0-3: diagonal block I of A and P and the inverse of I + A_II,
 //        kept in registers; waves 4-9: one pair of off-diagonal blocks of A
-//        and P; waves 10-15: the decay tables and K o e^-L transposed.
-//   YZ   wave (I, value tile): (K o e^G) S and (Q o e^G) S for its 16 rows and
-//        16 value columns, then R = B (V - (K o e^G) S).
+//        and P; waves 14-15: the decay tables.
+//   YZ   one wave per (row block I, pair of value tiles): (K o e^G) S and
+//        (Q o e^G) S for its 16 rows and 32 value columns, then
+//        R = B (V - (K o e^G) S).
 //   U    one wave per 16 value columns: the forward substitution.
-//   SO   every wave: its state tiles S' = Diag(gamma) S + Kbar^T U, and its
-//        (I, value tile) block of O = (Q o e^G) S + P U, stored to o.
+//   SO   the read-out waves: their two blocks of O = (Q o e^G) S + P U,
+//        stored to o; waves 8 ..: one state row tile each, S' = Diag(gamma) S +
+//        Kbar^T U, the state staying in their registers across chunks.  Kbar^T
+//        comes from the token-major K o e^{B-L} through the LDS transpose read.
 // Contractions run on the matrix cores (v_mfma_f32_16x16x32_bf16 and
 // v_mfma_f32_16x16x16_bf16, or v_mfma_f32_16x16x4_f32 for fp32 inputs) with
 // fp32 accumulation; operands are rounded to the input type.  The fp32 state
@@ -70,7 +73,8 @@ struct Cfg {
     static constexpr int NCT = DK / 16;               // state row tiles
     static constexpr int NVT = BV / 16;               // state column tiles
     static constexpr int NTILE = NCT * NVT;
-    static constexpr int NST = (NTILE + NW - 1) / NW; // state tiles per wave
+    static constexpr int SW0 = NW / 2;                // first state wave
+    static constexpr int NREG = NVT > 2 ? NVT : 2;    // f32x4 tiles held per wave
     static constexpr int NJOB = NB * NVT;             // (row block, value tile) jobs
     static constexpr int VEC = 8 / (int)sizeof(T);    // elements per 8-byte vector
     static constexpr int VPR = BV / VEC;              // 8-byte vectors per value row
@@ -78,7 +82,7 @@ struct Cfg {
     static_assert(DK % 32 == 0 && DK <= 128, "head size");
     static_assert(BV % 16 == 0 && NJOB <= NW, "value slice");
     static_assert(EWAVES <= NW, "elementwise mapping");
-    static_assert(NTILE <= NW || (NTILE % NW == 0 && NW % NCT == 0), "state tiling");
+    static_assert(NCT <= NW - SW0, "state tiling");
     static_assert(DK % Path<T>::KS == 0 && C % Path<T>::KS == 0, "k steps");
 };
 
@@ -87,9 +91,10 @@ struct Smem {
     typedef Cfg<T, DK, BV> Cf;
     T Kr[Cf::C][Cf::LDK];       // K o e^{L}         row operand
     T Qr[Cf::C][Cf::LDK];       // Q o e^{L}
-    T Kc[Cf::C][Cf::LDK];       // K o e^{B - L}     column operand, blocks J < I
+    T Kc[2][Cf::C][Cf::LDK];    // K o e^{B - L}     column operand, blocks J < I; two
+                                //                   buffers: the state update reads it
+                                //                   after the next chunk's E has run
     T Kd[Cf::C][Cf::LDK];       // K o e^{-L}        column operand, diagonal blocks
-    T KdT[DK][Cf::LDC];         // K o e^{-L}, [channel][token]
     T P[Cf::C][Cf::LDC];        // Tril((Q o e^G)(K o e^-G)^T)
     T An[Cf::C][Cf::LDC];       // -A, blocks J < I
     T Tm[Cf::NB][16][Cf::LD16]; // (I + A_II)^-1
@@ -98,7 +103,7 @@ struct Smem {
     T V[Cf::C][Cf::LDV];        // value slice
     float eB[Cf::NB][DK];       // e^{B_J}
     float eE[Cf::NB + 1][DK];   // prod_{m<J} e^{B_m}; row NB: whole-chunk decay
-    float eTi[Cf::NB][DK];      // prod_{m>=J} e^{B_m}
+    float eTx[Cf::NB][DK];      // prod_{m>J} e^{B_m}
     float beta[Cf::C];
     float nrm[2][Cf::C][Cf::WPB];  // fused prologue: partial sums of squares of k, q rows
     float bA[DK];                  // fused prologue: decay bias b_alpha^h of the head
@@ -128,14 +133,23 @@ struct SeqView {
     int v0;             // first value column of the slice
 };
 
-// Offset (in elements) of row `row` of the chunk, clamped to the last row of
-// the sequence: rows past the end read a valid address and are zeroed where
-// the values are consumed.  Offsets are 32-bit and added to a wave-uniform
-// base pointer, so that an access costs one VGPR.
-__device__ __forceinline__ uint32_t row_off(int row, int64_t nvalid, int rowstride)
+// Byte offset of element `col` of row `row` of the chunk, the row clamped to
+// `last`, the chunk's last row in the sequence: rows past the end read a valid
+// address and are zeroed where the values are consumed.  Offsets are 32-bit
+// and added to a wave-uniform 64-bit base, so that an access costs one VGPR
+// and no 64-bit vector arithmetic; the row stride in bytes is below 2^24 (the
+// launcher checks it), so that the product is one 24-bit multiply-add.
+template <typename E>
+__device__ __forceinline__ uint32_t row_byte_off(int row, int last, uint32_t stride_bytes, int col)
 {
-    const int r = row < nvalid ? row : (int)nvalid - 1;
-    return (uint32_t)r * (uint32_t)rowstride;
+    const uint32_t r = (uint32_t)min(row, last);
+    return __umul24(r, stride_bytes) + (uint32_t)col * (uint32_t)sizeof(E);
+}
+
+template <typename V, typename E>
+__device__ __forceinline__ V load_at(const E *base, uint32_t byte_off)
+{
+    return *reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
 // Loads are unconditional, so that no select on a loaded value makes the wave
@@ -154,21 +168,26 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
     typedef typename Vec<T>::two V2;
     typedef typename Vec<T>::eight_bytes V8;
     const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
-    const int64_t nvalid = sv.eos - t0;
+    const int64_t nvalid = sv.eos - t0;                    // >= 1
+    const int last = nvalid < Cf::C ? (int)nvalid - 1 : Cf::C - 1;
     const int64_t cbase = (t0 * sv.H + sv.head) * DK;      // wave-uniform
-    const int rs = sv.H * DK;                              // row stride, elements
+    const uint32_t rs = (uint32_t)(sv.H * DK);             // row stride, elements
+    const uint32_t rsT = rs * (uint32_t)sizeof(T), rsG = rs * 4u;
     if (wv < Cf::EWAVES) {
         const int I = wv / Cf::WPB, cp = (wv % Cf::WPB) * 16 + (lane & 15), qr = lane >> 4;
+        const float *gb = g + cbase;
+        const T *zb = z + cbase, *kb = k + cbase, *qb = q + cbase;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const uint32_t off = row_off(16 * I + 4 * qr + r, nvalid, rs) + 2 * cp;
+            const int row = 16 * I + 4 * qr + r;
             if (parts & LOAD_G) {
-                if (FUSED) R.z[r] = *reinterpret_cast<const V2 *>(z + cbase + off);
-                else R.g[r] = *reinterpret_cast<const f32x2 *>(g + cbase + off);
+                if (FUSED) R.z[r] = load_at<V2>(zb, row_byte_off<T>(row, last, rsT, 2 * cp));
+                else R.g[r] = load_at<f32x2>(gb, row_byte_off<float>(row, last, rsG, 2 * cp));
             }
             if (parts & LOAD_KQ) {
-                R.k[r] = *reinterpret_cast<const V2 *>(k + cbase + off);
-                R.q[r] = *reinterpret_cast<const V2 *>(q + cbase + off);
+                const uint32_t bo = row_byte_off<T>(row, last, rsT, 2 * cp);
+                R.k[r] = load_at<V2>(kb, bo);
+                R.q[r] = load_at<V2>(qb, bo);
             }
         }
     }
@@ -177,12 +196,12 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
 #pragma unroll
         for (int m = 0; m < Cf::NVV; ++m) {
             const int vi = t + Cf::NT * m;
-            const int row = (vi / Cf::VPR) < Cf::C ? vi / Cf::VPR : Cf::C - 1, cv = vi % Cf::VPR;
-            R.v[m] = *reinterpret_cast<const V8 *>(vb + row_off(row, nvalid, sv.H * DV) +
-                                                   cv * Cf::VEC);
+            const int row = min(vi / Cf::VPR, Cf::C - 1), cv = vi % Cf::VPR;
+            R.v[m] = load_at<V8>(vb, row_byte_off<T>(row, last, (uint32_t)(sv.H * DV * sizeof(T)),
+                                                      cv * Cf::VEC));
         }
         const float *bb = beta + t0 * sv.H + sv.head;
-        R.beta = bb[row_off(t < Cf::C ? t : 0, nvalid, sv.H)];
+        R.beta = load_at<float>(bb, row_byte_off<float>(t < Cf::C ? t : 0, last, (uint32_t)sv.H * 4u, 0));
     }
 }
 
@@ -261,7 +280,7 @@ __device__ __forceinline__ float bounded_alpha(float z, float eA, float b)
 // function table), whose partial sums of squares are in sm.nrm.
 template <bool FULL, bool FUSED, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
-                                        const GateCtx &gc)
+                                        const GateCtx &gc, int buf)
 {
     typedef Cfg<T, DK, BV> Cf;
     typedef typename Vec<T>::two V2;
@@ -339,7 +358,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
                 pack2<T>(kk[0] * eL[0][r], kk[1] * eL[1][r]);
             *reinterpret_cast<V2 *>(&sm.Qr[r0 + r][2 * cp]) =
                 pack2<T>(qq[0] * eL[0][r], qq[1] * eL[1][r]);
-            *reinterpret_cast<V2 *>(&sm.Kc[r0 + r][2 * cp]) = pack2<T>(kc[0], kc[1]);
+            *reinterpret_cast<V2 *>(&sm.Kc[buf][r0 + r][2 * cp]) = pack2<T>(kc[0], kc[1]);
             *reinterpret_cast<V2 *>(&sm.Kd[r0 + r][2 * cp]) = pack2<T>(kd[0], kd[1]);
         }
         if (qr == 0) *reinterpret_cast<f32x2 *>(&sm.eB[I][2 * cp]) = f32x2{ebv[0], ebv[1]};
@@ -356,10 +375,10 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
 
 template <bool FUSED, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
-                                        const GateCtx &gc)
+                                        const GateCtx &gc, int buf)
 {
-    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED>(sm, R, nv, gc);
-    else e_phase<false, FUSED>(sm, R, nv, gc);
+    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED>(sm, R, nv, gc, buf);
+    else e_phase<false, FUSED>(sm, R, nv, gc, buf);
 }
 
 // Sum over the 16 lanes of a row of the wave (lanes 16 j .. 16 j + 15), with
@@ -402,10 +421,10 @@ __device__ __forceinline__ void norm_partials(Smem<T, DK, BV> &sm, const ChunkRe
 // Off-diagonal blocks (I, J < I) of A (stored negated, beta applied) and of P.
 // The column operand K o e^{B_J - L_j} is brought to the reference of row
 // block I by prod_{J<m<I} e^{B_m} (nothing for adjacent blocks), once for
-// both products.  The products are taken
-// transposed so that each lane ends with four consecutive columns of one row.
+// both products.  The products are taken transposed so that each lane ends
+// with four consecutive columns of one row.
 template <int I, int J, typename T, int DK, int BV>
-__device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp)
+__device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp, int buf)
 {
     typedef Path<T> PT;
     typedef typename Vec<T>::four V4;
@@ -414,7 +433,7 @@ __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp)
 #pragma unroll
     for (int ks = 0; ks < DK / KS; ++ks) {
         const int kc = ks * KS + grp * KPL;
-        typename PT::frag col = load_frag<T>(&sm.Kc[16 * J + n16][kc]);
+        typename PT::frag col = load_frag<T>(&sm.Kc[buf][16 * J + n16][kc]);
         if (I > J + 1) {
             float x[KPL], f[KPL];
             PT::unpack(col, x);
@@ -446,31 +465,110 @@ __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp)
     *reinterpret_cast<V4 *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(wp);
 }
 
-// (K o e^G) S and (Q o e^G) S for row block I and value tile vt.  The decay
-// e^{E_I} from the chunk start to sub-block I scales the state operand (one
-// fragment serves both products).  Y comes back in the D layout (rows of the
-// block in 4 grp + i, value columns in n16); Z transposed (value columns in
-// 4 grp + i, rows in n16), as the output's transposed product needs it.
-template <bool SCALE, typename T, int DK, int BV>
-__device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt, int n16, int grp,
-                                         f32x4 &Y, f32x4 &Zt)
+// Decay tables of the chunk for channel c: e^{E_J} = prod_{m<J} e^{B_m}
+// (J = 0..NB, the last being the whole-chunk decay) and prod_{m>J} e^{B_m}.
+template <typename T, int DK, int BV>
+__device__ __forceinline__ void decay_tables(Smem<T, DK, BV> &sm, int c)
+{
+    constexpr int NB = Cfg<T, DK, BV>::NB;
+    float e[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) e[m] = sm.eB[m][c];
+    float f = 1.f;
+#pragma unroll
+    for (int m = 0; m <= NB; ++m) {
+        sm.eE[m][c] = f;
+        if (m < NB) f *= e[m];
+    }
+    f = 1.f;
+#pragma unroll
+    for (int m = NB - 1; m >= 0; --m) {
+        sm.eTx[m][c] = f;
+        f *= e[m];
+    }
+}
+
+// Operand fragment of X^T for a contraction over tokens, X stored token-major
+// in LDS (row stride ld): lane (n16, grp) receives X[k][c0 + n16] for the KPL
+// tokens k of its k group at k step k0.  For 16-bit data the LDS transpose
+// read of gfx950 (ds_read_b64_tr_b16) does it: within each group of 16 lanes,
+// lane n receives element i of lane 4 i + n / 4 at position n % 4, so lane
+// s = 4 i + j supplies the four channels c0 + 4 j .. c0 + 4 j + 3 of token i.
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf16 *p)
+{
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const s4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)p);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 load_frag_tr(const bf16 *x, int ld, int k0, int c0, int n16, int grp)
+{
+    const bf16 *p = x + (k0 + 8 * grp + (n16 >> 2)) * ld + c0 + 4 * (n16 & 3);
+    const bf16x4 lo = ds_read_tr4(p), hi = ds_read_tr4(p + 4 * ld);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ float load_frag_tr(const float *x, int ld, int k0, int c0, int n16, int grp)
+{
+    return x[(k0 + grp) * ld + c0 + n16];
+}
+
+// (K o e^G) S and (Q o e^G) S for row block I and the NV value tiles
+// vt0 .. vt0 + NV - 1.  The decay e^{E_I} from the chunk start to sub-block I
+// scales the state operand (one fragment serves both products); the decay
+// factors and the K, Q fragments of a k step serve every value tile.  Y comes
+// back in the D layout (rows of the block in 4 grp + i, value columns in n16);
+// Z transposed (value columns in 4 grp + i, rows in n16), as the output's
+// transposed product needs it.
+template <bool SCALE, int NV, typename T, int DK, int BV>
+__device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, int n16, int grp,
+                                         f32x4 (&Y)[NV], f32x4 (&Zt)[NV])
 {
     typedef Path<T> PT;
     constexpr int KS = PT::KS, KPL = PT::KPL;
 #pragma unroll
     for (int ks = 0; ks < DK / KS; ++ks) {
         const int kc = ks * KS + grp * KPL;
-        typename PT::frag s = load_frag<T>(&sm.ST[16 * vt + n16][kc]);
-        if (SCALE) {
-            float x[KPL], f[KPL];
-            PT::unpack(s, x);
-            load_f32<KPL>(f, &sm.eE[I][kc]);
+        float f[KPL];
+        if (SCALE) load_f32<KPL>(f, &sm.eE[I][kc]);
+        const typename PT::frag kr = load_frag<T>(&sm.Kr[16 * I + n16][kc]);
+        const typename PT::frag qr = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
 #pragma unroll
-            for (int e = 0; e < KPL; ++e) x[e] *= f[e];
-            s = PT::pack(x);
+        for (int v = 0; v < NV; ++v) {
+            typename PT::frag s = load_frag<T>(&sm.ST[16 * (vt0 + v) + n16][kc]);
+            if (SCALE) {
+                float x[KPL];
+                PT::unpack(s, x);
+#pragma unroll
+                for (int e = 0; e < KPL; ++e) x[e] *= f[e];
+                s = PT::pack(x);
+            }
+            Y[v] = PT::mma(kr, s, Y[v]);
+            Zt[v] = PT::mma(s, qr, Zt[v]);
         }
-        Y = PT::mma(load_frag<T>(&sm.Kr[16 * I + n16][kc]), s, Y);
-        Zt = PT::mma(s, load_frag<T>(&sm.Qr[16 * I + n16][kc]), Zt);
+    }
+}
+
+// State read-out of job (I, value tiles vt0 .. vt0 + NV - 1): Y and Z^T by
+// yz_block, then R = B (V - Y) stored transposed for the substitution.
+template <bool SCALE, int NV, typename T, int DK, int BV>
+__device__ __forceinline__ void readout_r(Smem<T, DK, BV> &sm, int I, int vt0, f32x4 (&Zt)[NV])
+{
+    typedef typename Vec<T>::four V4;
+    const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+    f32x4 Y[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) Y[v] = zero4();
+    yz_block<SCALE, NV>(sm, I, vt0, n16, grp, Y, Zt);
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * I + 4 * grp]);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int vt = vt0 + v;
+        float rv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            rv[i] = b4[i] * (to_f32(sm.V[16 * I + 4 * grp + i][16 * vt + n16]) - Y[v][i]);
+        *reinterpret_cast<V4 *>(&sm.RT[16 * vt + n16][16 * I + 4 * grp]) = pack4<T>(rv);
     }
 }
 
@@ -497,7 +595,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     typedef typename Vec<T>::four V4;
     constexpr int C = Cf::C, NB = Cf::NB, NT = Cf::NT, KS = PT::KS, KPL = PT::KPL;
     constexpr int NSLICE = DV / BV;
-    constexpr int NVT = Cf::NVT, NCT = Cf::NCT, NST = Cf::NST;
+    constexpr int NVT = Cf::NVT, NCT = Cf::NCT;
     __shared__ __align__(16) Sm sm;
 
     // ---- work item: (sequence, head, value slice); slices of one head adjacent
@@ -524,26 +622,27 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const int t = threadIdx.x;
     const int lane = lane_id(), wv = wave_id();
 
-    // ---- state tiles of this wave, D layout: tile (ct, vt) holds
-    // S[16 ct + 4 grp + i][16 vt + n16].  Tiles wv, wv + 16, ... share one ct.
-    const int ct = wv % NCT;
-    f32x4 S[NST];
+    // ---- register tiles W.  The state waves SW0 .. SW0 + NCT - 1 hold the
+    // state row tile ct = wv - SW0 for every value tile vt in W[vt], D layout:
+    // S[16 ct + 4 grp + i][16 vt + n16].  The read-out waves hold the
+    // transposed (Q o e^G) S of their two output blocks in W[0], W[1].
+    const bool state_wave = wv >= Cf::SW0 && wv < Cf::SW0 + NCT;
+    const int ct = wv - Cf::SW0;
+    f32x4 W[Cf::NREG];
+#pragma unroll
+    for (int v = 0; v < Cf::NREG; ++v) W[v] = zero4();
     const int64_t sbase = ((int64_t)seq * H + head) * (int64_t)(DK * DV) + sv.v0;
-    {
+    if (state_wave) {
         const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
-        for (int s = 0; s < NST; ++s) {
-            S[s] = zero4();
-            const int tl = wv + Cf::NW * s, vt = tl / NCT;
-            if (tl < Cf::NTILE) {
-                if (s0) {
+        for (int vt = 0; vt < NVT; ++vt) {
+            if (s0) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        S[s][i] = s0[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16];
-                }
-                float s4[4] = {S[s][0], S[s][1], S[s][2], S[s][3]};
-                *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
+                for (int i = 0; i < 4; ++i)
+                    W[vt][i] = s0[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16];
             }
+            float s4[4] = {W[vt][0], W[vt][1], W[vt][2], W[vt][3]};
+            *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
         }
     }
     // constant zero blocks above the diagonal of P
@@ -552,9 +651,15 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         if ((j >> 4) > (r >> 4)) sm.P[r][j] = from_f32<T>(0.f);
     }
 
-    // (row block, value tile) job of this wave in the YZ and output phases
-    const bool has_job = wv < Cf::NJOB;
-    const int jI = wv / NVT, jvt = wv % NVT;
+    // (row block, pair of value tiles) job of this wave for the state read-out
+    // and the output, on waves 0 .. NB NP - 1: row blocks 1 .. NB - 1 first,
+    // row block 0 (which needs no decay scaling) last, so that the SIMDs that
+    // get two jobs (waves w and w + 4 share a SIMD) mix light and heavy ones.
+    constexpr int NP = NVT / 2;
+    static_assert(NVT % 2 == 0 && NB * NP <= Cf::SW0, "job mapping");
+    const bool has_job = wv < NB * NP;
+    const int jI = wv < (NB - 1) * NP ? 1 + wv / NP : 0;
+    const int jvt = 2 * (wv % NP);                        // first of the two value tiles
 
     GateCtx gc;
     gc.eA = 1.f;
@@ -573,7 +678,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             norm_partials(sm, R);
             __syncthreads();
         }
-        e_phase<FUSED>(sm, R, rows_in(sv.bos, sv.eos, C), gc);
+        e_phase<FUSED>(sm, R, rows_in(sv.bos, sv.eos, C), gc, 0);
     }
     __syncthreads();
 
@@ -583,6 +688,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         const int64_t t0 = sv.bos + ch * C;
         const int nv = rows_in(t0, sv.eos, C);           // rows of this chunk in the sequence
         const bool more = ch + 1 < nchunks;
+        const int kbuf = (int)(ch & 1);                  // Kc buffer of this chunk
         if (more) load_chunk<FUSED>(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, z, beta, DV);
 
         // ================= AP
@@ -642,66 +748,28 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             // that the four SIMDs get similar shares
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
             switch (wv - NB) {
-                case 0: ap_pair<3, 0>(sm, n16, grp); break;
-                case 1: ap_pair<2, 0>(sm, n16, grp); break;
-                case 2: ap_pair<3, 1>(sm, n16, grp); break;
-                case 3: ap_pair<1, 0>(sm, n16, grp); break;
-                case 4: ap_pair<2, 1>(sm, n16, grp); break;
-                default: ap_pair<3, 2>(sm, n16, grp); break;
+                case 0: ap_pair<3, 0>(sm, n16, grp, kbuf); break;
+                case 1: ap_pair<2, 0>(sm, n16, grp, kbuf); break;
+                case 2: ap_pair<3, 1>(sm, n16, grp, kbuf); break;
+                case 3: ap_pair<1, 0>(sm, n16, grp, kbuf); break;
+                case 4: ap_pair<2, 1>(sm, n16, grp, kbuf); break;
+                default: ap_pair<3, 2>(sm, n16, grp, kbuf); break;
             }
-        } else {
-            // decay tables, one channel per thread; then K o e^-L transposed,
-            // for the state update (two channels by four tokens per task)
-            typedef typename Vec<T>::two V2;
-            const int tw = 64 * (wv - NB - 6) + opaque_lane();
-            const int c = tw;
-            for (int task = tw; task < (DK / 2) * (C / 4); task += 64 * (Cf::NW - NB - 6)) {
-                const int cpair = task % (DK / 2), tq = task / (DK / 2);
-                float x[2][4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const V2 d2 = *reinterpret_cast<const V2 *>(&sm.Kd[4 * tq + r][2 * cpair]);
-                    x[0][r] = to_f32(d2[0]);
-                    x[1][r] = to_f32(d2[1]);
-                }
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-                    *reinterpret_cast<V4 *>(&sm.KdT[2 * cpair + cc][4 * tq]) = pack4<T>(x[cc]);
-            }
-            if (c < DK) {
-                float e[NB];
-#pragma unroll
-                for (int m = 0; m < NB; ++m) e[m] = sm.eB[m][c];
-                float f = 1.f;
-#pragma unroll
-                for (int m = 0; m <= NB; ++m) {
-                    sm.eE[m][c] = f;
-                    if (m < NB) f *= e[m];
-                }
-                f = 1.f;
-#pragma unroll
-                for (int m = NB - 1; m >= 0; --m) {
-                    f *= e[m];
-                    sm.eTi[m][c] = f;
-                }
-            }
+        } else if (wv >= Cf::NW - 2) {
+            // decay tables, one channel per thread
+            const int c = 64 * (wv - (Cf::NW - 2)) + opaque_lane();
+            if (c < DK) decay_tables(sm, c);
         }
         __syncthreads();   // ---------------------------------------------- B1
         if (more) load_chunk<FUSED>(R, LOAD_VB, sv, t0 + C, q, k, v, g, z, beta, DV);
 
-        // ================= YZ: state read-out and R = B (V - Y), stored transposed
-        f32x4 Zt = zero4();
+        // ================= YZ: state read-out for row blocks 1.. and R = B (V - Y)
         if (has_job) {
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
-            f32x4 Y = zero4();
-            if (jI == 0) yz_block<false>(sm, 0, jvt, n16, grp, Y, Zt);
-            else yz_block<true>(sm, jI, jvt, n16, grp, Y, Zt);
-            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * jI + 4 * grp]);
-            float rv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                rv[i] = b4[i] * (to_f32(sm.V[16 * jI + 4 * grp + i][16 * jvt + n16]) - Y[i]);
-            *reinterpret_cast<V4 *>(&sm.RT[16 * jvt + n16][16 * jI + 4 * grp]) = pack4<T>(rv);
+            f32x4 (&Zt)[2] = *reinterpret_cast<f32x4 (*)[2]>(&W[0]);
+            Zt[0] = zero4();
+            Zt[1] = zero4();
+            if (jI > 0) readout_r<true, 2>(sm, jI, jvt, Zt);
+            else readout_r<false, 2>(sm, 0, jvt, Zt);
         }
         // fused prologue: the next chunk's row norms, read by its E after B2
         if (FUSED && more) norm_partials(sm, R);
@@ -733,22 +801,23 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         }
         // ================= the next chunk's elementwise phase (the substituting
         // waves do their share after their substitution)
-        if (more) e_phase<FUSED>(sm, R, rows_in(t0 + C, sv.eos, C), gc);
+        if (more) e_phase<FUSED>(sm, R, rows_in(t0 + C, sv.eos, C), gc, kbuf ^ 1);
         __syncthreads();   // ---------------------------------------------- B3
 
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
-        if (wv < Cf::NTILE) {
+        if (state_wave) {
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
-            // (K o e^{G_n - G})^T fragments of this wave's state row tile
+            // (K o e^{G_n - G})^T fragments of this wave's state row tile:
+            // (K o e^{B - L}) read transposed, times prod_{m>J} e^{B_m}
             typename PT::frag kb[C / KS];
             {
                 const int c = 16 * ct + n16;
 #pragma unroll
                 for (int ks = 0; ks < C / KS; ++ks) {
                     const int kj = ks * KS + grp * KPL;
-                    const float f = sm.eTi[kj >> 4][c];
+                    const float f = sm.eTx[kj >> 4][c];
                     float x[KPL];
-                    PT::unpack(load_frag<T>(&sm.KdT[c][kj]), x);
+                    PT::unpack(load_frag_tr(&sm.Kc[kbuf][0][0], Cf::LDK, ks * KS, 16 * ct, n16, grp), x);
 #pragma unroll
                     for (int e = 0; e < KPL; ++e) x[e] *= f;
                     kb[ks] = PT::pack(x);
@@ -756,50 +825,52 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             }
             const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[NB][16 * ct + 4 * grp]);
 #pragma unroll
-            for (int s = 0; s < NST; ++s) {
-                const int vt = (wv + Cf::NW * s) / NCT;
-                f32x4 acc = S[s] * gam;
+            for (int vt = 0; vt < NVT; ++vt) {
+                f32x4 acc = W[vt] * gam;
 #pragma unroll
                 for (int ks = 0; ks < C / KS; ++ks) {
                     const int kj = ks * KS + grp * KPL;
                     acc = PT::mma(kb[ks], load_frag<T>(&sm.RT[16 * vt + n16][kj]), acc);
                 }
-                S[s] = acc;
+                W[vt] = acc;
                 float s4[4] = {acc[0], acc[1], acc[2], acc[3]};
                 *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
             }
         }
         if (has_job) {
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
-            // transposed block: lane holds O[16 jI + n16][16 jvt + 4 grp + i]
+            // transposed blocks: lane holds O[16 jI + n16][16 (jvt + v) + 4 grp + i]
             const int nks = (16 * (jI + 1) + KS - 1) / KS;
-            f32x4 acc = Zt;
+            f32x4 acc[2] = {W[0], W[1]};
             for (int ks = 0; ks < nks; ++ks) {
                 const int kj = ks * KS + grp * KPL;
-                acc = PT::mma(load_frag<T>(&sm.RT[16 * jvt + n16][kj]),
-                              load_frag<T>(&sm.P[16 * jI + n16][kj]), acc);
+                const typename PT::frag pf = load_frag<T>(&sm.P[16 * jI + n16][kj]);
+#pragma unroll
+                for (int v = 0; v < 2; ++v)
+                    acc[v] = PT::mma(load_frag<T>(&sm.RT[16 * (jvt + v) + n16][kj]), pf, acc[v]);
             }
             const int row = 16 * jI + n16;
             if (row < nv) {
                 T *ob = o + (t0 * H + head) * DV + sv.v0;         // wave-uniform
-                float o4[4] = {acc[0], acc[1], acc[2], acc[3]};
-                *reinterpret_cast<V4 *>(ob + (uint32_t)row * (uint32_t)(H * DV) + 16 * jvt +
-                                        4 * grp) = pack4<T>(o4);
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    float o4[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
+                    const uint32_t bo = __umul24((uint32_t)row, (uint32_t)(H * DV * sizeof(T))) +
+                                        (uint32_t)((16 * (jvt + v) + 4 * grp) * sizeof(T));
+                    *reinterpret_cast<V4 *>(reinterpret_cast<char *>(ob) + bo) = pack4<T>(o4);
+                }
             }
         }
         __syncthreads();   // ---------------------------------------------- B4
     }
 
-    if (sfinal) {
+    if (sfinal && state_wave) {
         const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
-        for (int s = 0; s < NST; ++s) {
-            const int tl = wv + Cf::NW * s, vt = tl / NCT;
-            if (tl < Cf::NTILE) {
+        for (int vt = 0; vt < NVT; ++vt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sfinal[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16] = S[s][i];
-            }
+            for (int i = 0; i < 4; ++i)
+                sfinal[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16] = W[vt][i];
         }
     }
 }
@@ -813,6 +884,8 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 {
     const int64_t nwork = (int64_t)num_seqs * H * (D / BV);
     if (nwork == 0) return hipSuccess;
+    // token row strides in bytes (fp32 g is the widest) must fit 24 bits
+    if ((int64_t)H * D * 4 >= (int64_t)1 << 24) return hipErrorInvalidValue;
     hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FUSED>), dim3((unsigned)nwork),
                        dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)q, (const T *)k,
                        (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (T *)o, sf,
