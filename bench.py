@@ -113,7 +113,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
     res["prefill_fused_prologue"] = {
         "workload": w.name, "ms_per_step": ms, "tokens/s": n_tok / (ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": _gbs(fb, ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": _gbs(fb, ms) / HBM_PEAK_GBS, "traffic": None,
+                     "frac": _gbs(fb, ms) / HBM_PEAK_GBS,
+                     "traffic": _traffic("kda_prefill.hip", "k3_prefill_8k_fused_prologue"),
                      "kernel": "kda::prefill_kernel<..., fused prologue>", "bytes_per_launch": fb}}
     # output epilogue on the prefill's output rows
     rows = n_tok * w.H
@@ -124,7 +125,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
     res["output_gate"] = {"rows": rows, "d_v": w.dv, "ms_per_step": ms, "GB/s": _gbs(ob, ms),
                           "roofline": {"bound": "hbm", "achieved": _gbs(ob, ms),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": _gbs(ob, ms) / HBM_PEAK_GBS, "traffic": None,
+                                       "frac": _gbs(ob, ms) / HBM_PEAK_GBS,
+                                       "traffic": _traffic("kda_layer.hip", "output_gate_k3_8k"),
                                        "kernel": "kda::output_gate_kernel",
                                        "bytes_per_launch": ob}}
     # ShortConv over one projection (H * d_k channels), with streaming state
@@ -137,7 +139,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                          "GB/s": _gbs(cb, ms),
                          "roofline": {"bound": "hbm", "achieved": _gbs(cb, ms),
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": _gbs(cb, ms) / HBM_PEAK_GBS, "traffic": None,
+                                      "frac": _gbs(cb, ms) / HBM_PEAK_GBS,
+                                      "traffic": _traffic("kda_layer.hip", "short_conv_k3_8k"),
                                       "kernel": "kda::short_conv_kernel (+ state update)",
                                       "bytes_per_launch": cb}}
     del li, o, og, xc, st
@@ -179,7 +182,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                               "tokens/s": nt / (ms * 1e-3),
                               "roofline": {"bound": "hbm", "achieved": _gbs(nb, ms),
                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                           "frac": _gbs(nb, ms) / HBM_PEAK_GBS, "traffic": None,
+                                           "frac": _gbs(nb, ms) / HBM_PEAK_GBS,
+                                           "traffic": _traffic("kda_prefill.hip", "nano_k3_prefill"),
                                            "kernel": "kda::prefill_kernel<bf16, 64, 64>",
                                            "bytes_per_launch": nb}}
     del xn, on, sfn
@@ -192,7 +196,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
     res["nano_k3_decode"] = {"workload": wd.name, "ms_per_step": ms, "GB/s": _gbs(db, ms),
                              "roofline": {"bound": "hbm", "achieved": _gbs(db, ms),
                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                          "frac": _gbs(db, ms) / HBM_PEAK_GBS, "traffic": None,
+                                          "frac": _gbs(db, ms) / HBM_PEAK_GBS,
+                                          "traffic": _traffic("kda_decode.hip", "nano_k3_decode"),
                                           "kernel": "kda::decode_kernel<bf16, 64>",
                                           "bytes_per_launch": db}}
     return res
