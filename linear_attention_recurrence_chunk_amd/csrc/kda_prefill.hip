@@ -653,8 +653,9 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
 
     // (row block, pair of value tiles) job of this wave for the state read-out
     // and the output, on waves 0 .. NB NP - 1: row blocks 1 .. NB - 1 first,
-    // row block 0 (which needs no decay scaling) last, so that the SIMDs that
-    // get two jobs (waves w and w + 4 share a SIMD) mix light and heavy ones.
+    // row block 0 (which needs no decay scaling) last.  Waves w and w + 4 share
+    // a SIMD, so with 64-column value slices (eight jobs) two SIMDs get two
+    // rescaled jobs and the other two one rescaled and one light job.
     constexpr int NP = NVT / 2;
     static_assert(NVT % 2 == 0 && NB * NP <= Cf::SW0, "job mapping");
     const bool has_job = wv < NB * NP;
