@@ -107,12 +107,15 @@ __device__ __forceinline__ int seq_of(int64_t tok, const int32_t *__restrict__ c
     return lo;
 }
 
-// A thread owns four consecutive channels and a run of RUN consecutive tokens
-// and slides a three-input window along them, so that every input is read
-// once: a wave covers 64 channel quads of the same tokens (512 contiguous
-// bytes per bf16 access).  The window restarts at each sequence start, from
-// the streaming state or from zeros.
-template <typename T, int RUN>
+// A thread owns VEC consecutive channels (16 bytes of a row when C allows,
+// else 4) and a run of RUN consecutive tokens; a wave covers 64 channel groups
+// of the same tokens.  When the run and the three inputs before it lie in one
+// sequence (the common case), the thread loads those RUN + 3 rows at once and
+// then writes its RUN outputs, so that every load is in flight together.
+// Otherwise it slides a three-input window along the run, restarting it at
+// each sequence start from the streaming state or from zeros.  Either way
+// every input is read once per run, plus the three-row halo.
+template <typename T, int VEC, int RUN>
 __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x,
                                                          const float *__restrict__ w,
                                                          const int32_t *__restrict__ cu,
@@ -121,17 +124,18 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x
                                                          const float *__restrict__ state,
                                                          T *__restrict__ y)
 {
-    typedef T vec4 __attribute__((ext_vector_type(4)));
-    const int cq = C / 4;
-    const int quad = blockIdx.x * 64 + (threadIdx.x & 63);
-    if (quad >= cq) return;
-    const int c0 = quad * 4;
-    const int64_t t0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * RUN;
+    typedef T vecT __attribute__((ext_vector_type(VEC)));
+    typedef float vecF __attribute__((ext_vector_type(VEC)));
+    const int ng = C / VEC;
+    const int grp = blockIdx.x * 64 + (threadIdx.x & 63);
+    if (grp >= ng) return;
+    const int c0 = grp * VEC;
+    const int64_t t0 = ((int64_t)blockIdx.y * 4 + (threadIdx.x >> 6)) * RUN;   // wave-uniform
     if (t0 >= ntok) return;
     const int64_t t1 = t0 + RUN < ntok ? t0 + RUN : ntok;
-    float wt[4][4];                                  // wt[e][i]: channel c0 + e, tap i
+    float wt[VEC][4];                                // wt[e][i]: channel c0 + e, tap i
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < VEC; ++e) {
         const f32x4 ww = *reinterpret_cast<const f32x4 *>(w + (c0 + e) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) wt[e][i] = ww[i];
@@ -139,19 +143,42 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x
     int n = seq_of(t0, cu, nseq, seq_len);
     int64_t bos = cu ? (int64_t)cu[n] : (int64_t)n * seq_len;
     int64_t eos = cu ? (int64_t)cu[n + 1] : bos + seq_len;
+
+    if (t0 - 3 >= bos && t1 == t0 + RUN && t1 <= eos) {
+        // rows t0 - 3 .. t1 - 1 from a wave-uniform base, 32-bit lane offsets
+        const char *xb = reinterpret_cast<const char *>(x + (t0 - 3) * C);
+        char *yb = reinterpret_cast<char *>(y + t0 * C);
+        const uint32_t rowb = (uint32_t)C * (uint32_t)sizeof(T), cb = (uint32_t)c0 * (uint32_t)sizeof(T);
+        vecT xs[RUN + 3];
+#pragma unroll
+        for (int j = 0; j < RUN + 3; ++j)
+            xs[j] = *reinterpret_cast<const vecT *>(xb + (uint32_t)j * rowb + cb);
+#pragma unroll
+        for (int t = 0; t < RUN; ++t) {
+            vecT out;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                out[e] = from_f32<T>(wt[e][0] * to_f32(xs[t][e]) + wt[e][1] * to_f32(xs[t + 1][e]) +
+                                     wt[e][2] * to_f32(xs[t + 2][e]) + wt[e][3] * to_f32(xs[t + 3][e]));
+            __builtin_nontemporal_store(out, reinterpret_cast<vecT *>(yb + (uint32_t)t * rowb + cb));
+        }
+        return;
+    }
+
     // window[j]: input x_{t-3+j} for the next token t, j = 0..2
-    f32x4 win[3];
+    vecF win[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const int64_t src = t0 - 3 + j;
         if (src >= bos) {
-            const vec4 xx = *reinterpret_cast<const vec4 *>(x + src * C + c0);
+            const vecT xx = *reinterpret_cast<const vecT *>(x + src * C + c0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) win[j][e] = to_f32(xx[e]);
+            for (int e = 0; e < VEC; ++e) win[j][e] = to_f32(xx[e]);
         } else if (state) {
-            win[j] = *reinterpret_cast<const f32x4 *>(state + ((int64_t)n * 3 + j + (t0 - bos)) * C + c0);
+            win[j] = *reinterpret_cast<const vecF *>(state + ((int64_t)n * 3 + j + (t0 - bos)) * C + c0);
         } else {
-            win[j] = zero4();
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) win[j][e] = 0.f;
         }
     }
     for (int64_t t = t0; t < t1; ++t) {
@@ -160,20 +187,25 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x
             bos = eos;
             eos = cu ? (int64_t)cu[n + 1] : bos + seq_len;
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
-                win[j] = state ? *reinterpret_cast<const f32x4 *>(state + ((int64_t)n * 3 + j) * C + c0)
-                               : zero4();
+            for (int j = 0; j < 3; ++j) {
+                if (state) {
+                    win[j] = *reinterpret_cast<const vecF *>(state + ((int64_t)n * 3 + j) * C + c0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) win[j][e] = 0.f;
+                }
+            }
         }
-        const vec4 xx = *reinterpret_cast<const vec4 *>(x + t * C + c0);
-        f32x4 cur;
+        const vecT xx = *reinterpret_cast<const vecT *>(x + t * C + c0);
+        vecF cur;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cur[e] = to_f32(xx[e]);
-        vec4 out;
+        for (int e = 0; e < VEC; ++e) cur[e] = to_f32(xx[e]);
+        vecT out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < VEC; ++e)
             out[e] = from_f32<T>(wt[e][0] * win[0][e] + wt[e][1] * win[1][e] +
                                  wt[e][2] * win[2][e] + wt[e][3] * cur[e]);
-        *reinterpret_cast<vec4 *>(y + t * C + c0) = out;
+        *reinterpret_cast<vecT *>(y + t * C + c0) = out;
         win[0] = win[1];
         win[1] = win[2];
         win[2] = cur;
@@ -220,14 +252,22 @@ static hipError_t launch_short_conv_t(const void *x, const float *w, const int32
                                       int64_t ntok, int C, float *state, void *y,
                                       hipStream_t stream)
 {
-    constexpr int RUN = 16;
+    constexpr int RUN = 16, VEC = 16 / (int)sizeof(T);
     const int64_t seq_len = cu ? 0 : ntok / nseq;
     if (ntok > 0) {
         const int64_t gy = (ntok + 4 * RUN - 1) / (4 * RUN);
         if (gy > 65535) return hipErrorInvalidValue;   // grid y limit: 4.19 M tokens per call
-        const dim3 grid((unsigned)((C / 4 + 63) / 64), (unsigned)gy);
-        hipLaunchKernelGGL((short_conv_kernel<T, RUN>), grid, dim3(256), 0, stream,
-                           (const T *)x, w, cu, nseq, seq_len, ntok, C, state, (T *)y);
+        // the fast path's 32-bit offsets: RUN + 3 rows of C elements
+        if ((int64_t)(RUN + 3) * C * (int64_t)sizeof(T) >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+        if (C % VEC == 0) {
+            const dim3 grid((unsigned)((C / VEC + 63) / 64), (unsigned)gy);
+            hipLaunchKernelGGL((short_conv_kernel<T, VEC, RUN>), grid, dim3(256), 0, stream,
+                               (const T *)x, w, cu, nseq, seq_len, ntok, C, state, (T *)y);
+        } else {
+            const dim3 grid((unsigned)((C / 4 + 63) / 64), (unsigned)gy);
+            hipLaunchKernelGGL((short_conv_kernel<T, 4, RUN>), grid, dim3(256), 0, stream,
+                               (const T *)x, w, cu, nseq, seq_len, ntok, C, state, (T *)y);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -119,10 +119,10 @@ def test_output_gate(dtype, d, tol):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("with_state", [False, True])
-def test_short_conv_prefill(dtype, with_state):
+@pytest.mark.parametrize("C", [96, 100])     # 100: bf16 rows not a multiple of 16 bytes
+def test_short_conv_prefill(dtype, with_state, C):
     gen = torch.Generator(device=dev).manual_seed(3)
     lens = [5, 0, 1, 2, 300, 64]
-    C = 96
     n = sum(lens)
     x = torch.randn(n, C, generator=gen, device=dev).to(dtype)
     w = torch.randn(C, 4, generator=gen, device=dev)
@@ -133,7 +133,7 @@ def test_short_conv_prefill(dtype, with_state):
     torch.cuda.synchronize()
     y_ref, st_ref = L.short_conv(_np(x), _np(w), cu_seqlens=cu.cpu().numpy(), conv_state=st_in)
     e = _rel(_np(y), y_ref)
-    print(f"[parity] short conv {dtype} state={with_state}: {e:.3e}")
+    print(f"[parity] short conv {dtype} C={C} state={with_state}: {e:.3e}")
     assert e <= (1e-2 if dtype == torch.bfloat16 else 1e-6)
     if with_state:
         np.testing.assert_array_equal(_np(st), st_ref)    # copies of inputs: exact
