@@ -598,12 +598,19 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     constexpr int NVT = Cf::NVT, NCT = Cf::NCT;
     __shared__ __align__(16) Sm sm;
 
-    // ---- work item: (sequence, head, value slice); slices of one head adjacent
-    // and, when the count allows, on one XCD (workgroups are dealt to the 8 XCDs
-    // round-robin), so that they share q, k, g through that XCD's L2.
+    // ---- work item w = NSLICE (sequence H + head) + slice.  Workgroups are
+    // dealt to the 8 XCDs round-robin (block b to XCD b mod 8).  When the count
+    // allows, the slices of one head go to blocks of one residue mod 8, so that
+    // they share q, k, g through that XCD's L2, and consecutive heads go to
+    // consecutive XCDs, so that every XCD gets a share of every sequence
+    // whatever the mix of sequence lengths.
     const int64_t nwork = (int64_t)num_seqs * H * NSLICE;
     const int64_t b = blockIdx.x;
-    const int64_t w = (nwork % 8 == 0) ? (b % 8) * (nwork / 8) + b / 8 : b;
+    int64_t w = b;
+    if (nwork % (8 * NSLICE) == 0) {
+        const int64_t q8 = b / (8 * NSLICE), r8 = b % (8 * NSLICE);
+        w = NSLICE * (8 * q8 + r8 % 8) + r8 / 8;
+    }
     const int seq = (int)(w / ((int64_t)H * NSLICE));
     const int head = (int)((w / NSLICE) % H);
     const int slice = (int)(w % NSLICE);
