@@ -98,6 +98,8 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  *                                                       may alias initial_state
  *   workspace     device scratch of at least kda_chunk_fwd_workspace_size(...)
  *                 bytes (may be NULL when that size is 0).
+ * Limits: H * d_k * 4 < 2^24 (one token's fp32 g row below 16 MiB), else
+ * KDA_ERR_SHAPE.
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *initial_state,
@@ -183,8 +185,9 @@ kda_status kda_output_gate(const void *o_raw, const void *gate, const float *wei
  *               nothing written.  A decode step is a call with num_seqs
  *               sequences of one token each.
  *   y           [total_tokens][channels] dtype; must not alias x.
- * channels must be a multiple of 4.  Two launches on `stream` (the output,
- * then the state update).
+ * channels must be a multiple of 4; total_tokens <= 65535 * 64 and
+ * channels * 76 < 2^32 (else KDA_ERR_SHAPE).  Two launches on `stream` (the
+ * output, then the state update).
  */
 kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,
                           int32_t num_seqs, int64_t total_tokens, int32_t channels,

@@ -58,6 +58,9 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_SHAPE;
     if (!cu && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_SHAPE;
     if ((int64_t)num_seqs * H * 2 > INT32_MAX) return KDA_ERR_SHAPE;
+    // the kernel forms row offsets as 24-bit products: one token's fp32 g row
+    // (H d_k 4 bytes) must stay below 2^24 bytes
+    if ((int64_t)H * d_k * 4 >= ((int64_t)1 << 24)) return KDA_ERR_SHAPE;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
         misaligned(s0) || misaligned(cu) || misaligned(o) || misaligned(sf) || misaligned(ws))
@@ -147,6 +150,9 @@ kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_
     if (channels % 4 != 0) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_SHAPE;
     if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_SHAPE;
+    // grid limit (65535 blocks of 64 tokens) and the 32-bit offsets of 19 rows
+    if (total_tokens > (int64_t)65535 * 64 || (int64_t)channels * 19 * 4 >= ((int64_t)1 << 32))
+        return KDA_ERR_SHAPE;
     if (num_seqs == 0) return KDA_OK;
     if (!weight || (total_tokens > 0 && (!x || !y))) return KDA_ERR_NULL;
     if (misaligned(x) || misaligned(weight) || misaligned(cu_seqlens) || misaligned(conv_state) ||

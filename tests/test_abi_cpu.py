@@ -85,6 +85,7 @@ def _dec(**kw):
     (dict(dk=48, dv=48), EUNSUP), (dict(dk=64, dv=128), EUNSUP), (dict(dk=256, dv=256), EUNSUP),
     (dict(chunk=32), EUNSUP), (dict(chunk=96), EUNSUP), (dict(chunk=256), EUNSUP), (dict(dt=7), EUNSUP),
     (dict(dt=0, dk=128, dv=128), EUNSUP),            # fp32 path is for d <= 64
+    (dict(H=32768, dk=128, dv=128), ESHAPE),         # a token's g row must stay below 16 MiB
     (dict(q=MIS), EALIGN), (dict(g=MIS), EALIGN), (dict(o=MIS), EALIGN),
     (dict(s0=MIS), EALIGN), (dict(sf=MIS), EALIGN), (dict(cu=MIS), EALIGN),
 ])
@@ -164,6 +165,7 @@ def test_layer_steps_reject():
     assert lib.kda_short_conv(p(A), None, None, 2, 10, 8, None, p(A), 1, None) == ENULL
     assert lib.kda_short_conv(p(A), p(A), None, 2, 10, 8, p(MIS), p(A), 1, None) == EALIGN
     assert lib.kda_short_conv(p(A), p(A), None, 0, 0, 8, None, p(A), 1, None) == OK
+    assert lib.kda_short_conv(p(A), p(A), None, 1, 65535 * 64 + 1, 8, None, p(A), 1, None) == ESHAPE
     # state compose: square states of a supported size
     assert lib.kda_state_compose(p(A), p(A), p(A), p(A), 4, 64, 32, None) == EUNSUP
     assert lib.kda_state_compose(p(A), p(A), p(A), p(A), -1, 64, 64, None) == ESHAPE
