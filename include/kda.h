@@ -93,9 +93,16 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  *                 form is exact for any block size; this implementation advances
  *                 the state every 64 tokens for both values.
  *   o             [total_tokens][H][d_v]  dtype         o_t = S_t^T q_t; must not
- *                                                       alias an input
+ *                                                       alias an input.  May be
+ *                                                       NULL when final_state is
+ *                                                       not: only the states are
+ *                                                       computed and q is not read
+ *                                                       (it may then be NULL too)
  *   final_state   [num_seqs][H][d_k][d_v] fp32 or NULL  state after each sequence;
  *                                                       may alias initial_state
+ *   v may be NULL, standing for zero values: with initial_state = I (d_v = d_k)
+ *   and o = NULL the final state is then the transition product of each
+ *   sequence ("Glossaire", entry "KCP": the segment summary M).
  *   workspace     device scratch of at least kda_chunk_fwd_workspace_size(...)
  *                 bytes (may be NULL when that size is 0).
  * Limits: H * d_k * 4 < 2^24 (one token's fp32 g row below 16 MiB), else

@@ -96,12 +96,12 @@ def workspace_size(num_seqs: int, total_tokens: int, H: int, d: int, chunk_size:
                                                       chunk_size, _DTYPES[dtype]))
 
 
-def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tensor],
+              g: torch.Tensor, beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              final_state: Optional[torch.Tensor] = None, output: bool = True
+              ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Chunkwise KDA prefill (kda_chunk_fwd).
 
     q, k [N_tok, H, d_k] or [B, T, H, d_k]; v like q with d_v; g like q (fp32);
@@ -109,52 +109,64 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     None; cu_seqlens int32 [N + 1] on the device or None (one sequence per
     batch row).  Returns (o shaped like v, final_state [N, H, d_k, d_v] fp32 or
     None).  ``out`` / ``final_state`` may be passed preallocated.
+
+    output=False computes only the final states (o is None and q may be None);
+    v=None stands for zero values (d_v = d_k).
     """
-    if q.dtype not in _DTYPES:
-        raise ValueError(f"q must be bf16 or fp32, got {q.dtype}")
-    dev = q.device
-    _need(q, "q", ndim=(3, 4))
-    for name, x in (("k", k), ("v", v)):
-        _need(x, name, dtype=q.dtype, ndim=(q.dim(),), device=dev)
-    _need(g, "g", dtype=torch.float32, ndim=(q.dim(),), device=dev)
-    _need(beta, "beta", dtype=torch.float32, ndim=(q.dim() - 1,), device=dev)
-    if q.dim() == 4:
-        B, T = q.shape[:2]
+    if not output and not output_final_state and final_state is None:
+        raise ValueError("nothing to compute: output=False needs the final state")
+    if output and q is None:
+        raise ValueError("q is required when the output is computed")
+    if k.dtype not in _DTYPES:
+        raise ValueError(f"k must be bf16 or fp32, got {k.dtype}")
+    dev = k.device
+    _need(k, "k", ndim=(3, 4))
+    if q is not None:
+        _need(q, "q", dtype=k.dtype, ndim=(k.dim(),), device=dev)
+    if v is not None:
+        _need(v, "v", dtype=k.dtype, ndim=(k.dim(),), device=dev)
+    _need(g, "g", dtype=torch.float32, ndim=(k.dim(),), device=dev)
+    _need(beta, "beta", dtype=torch.float32, ndim=(k.dim() - 1,), device=dev)
+    if k.dim() == 4:
+        B, T = k.shape[:2]
         if cu_seqlens is not None:
             raise ValueError("cu_seqlens is only accepted with packed 3-D inputs")
         num_seqs, n_tok = B, B * T
     else:
-        n_tok = q.shape[0]
+        n_tok = k.shape[0]
         if cu_seqlens is None:
             num_seqs = 1
         else:
             _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=(1,), device=dev)
             num_seqs = cu_seqlens.shape[0] - 1
-    H, dk = q.shape[-2:]
-    dv = v.shape[-1]
-    if k.shape != q.shape or g.shape != q.shape or v.shape[:-1] != q.shape[:-1]:
+    H, dk = k.shape[-2:]
+    dv = dk if v is None else v.shape[-1]
+    if (q is not None and q.shape != k.shape) or g.shape != k.shape or \
+            (v is not None and v.shape[:-1] != k.shape[:-1]):
         raise ValueError("q, k, g must share a shape and v must match it up to d_v")
-    if beta.shape != q.shape[:-1]:
-        raise ValueError(f"beta must have shape {tuple(q.shape[:-1])}")
+    if beta.shape != k.shape[:-1]:
+        raise ValueError(f"beta must have shape {tuple(k.shape[:-1])}")
     sshape = (num_seqs, H, dk, dv)
     if initial_state is not None:
         _need(initial_state, "initial_state", dtype=torch.float32, device=dev)
         if tuple(initial_state.shape) != sshape:
             raise ValueError(f"initial_state must have shape {sshape}")
-    if out is None:
-        out = torch.empty_like(v)
+    if not output:
+        out = None
+    elif out is None:
+        out = torch.empty(k.shape[:-1] + (dv,), dtype=k.dtype, device=dev)
     else:
-        _need(out, "out", dtype=v.dtype, device=dev)
+        _need(out, "out", dtype=k.dtype, device=dev)
     if final_state is None and output_final_state:
         final_state = torch.empty(sshape, dtype=torch.float32, device=dev)
     elif final_state is not None:
         _need(final_state, "final_state", dtype=torch.float32, device=dev)
-    ws_bytes = workspace_size(num_seqs, n_tok, H, dk, chunk_size, q.dtype)
+    ws_bytes = workspace_size(num_seqs, n_tok, H, dk, chunk_size, k.dtype)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     lib = library()
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                            _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv, chunk_size,
-                           _DTYPES[q.dtype], _ptr(out), _ptr(final_state), _ptr(ws), ws_bytes,
+                           _DTYPES[k.dtype], _ptr(out), _ptr(final_state), _ptr(ws), ws_bytes,
                            _stream(dev))
     _check("kda_chunk_fwd", st)
     return out, final_state
@@ -315,15 +327,16 @@ def state_compose(M: torch.Tensor, S_in: torch.Tensor, S_tilde: torch.Tensor,
 def kcp_summaries(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, cu_seqlens: torch.Tensor
                   ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Per-segment summaries (M, S~) of packed segments, each with two
-    kda_chunk_fwd launches over all segments at once: S~ from S = 0, and M
-    from S = I with v = 0 (d_v = d_k).  Returns ([P, H, d, d], [P, H, d, d_v])."""
+    """Per-segment summaries (M, S~) of packed segments, each with one
+    state-only kda_chunk_fwd launch over all segments at once: S~ from S = 0,
+    and M from S = I with zero values (d_v = d_k).  q is not needed.
+    Returns ([P, H, d, d], [P, H, d, d_v])."""
     P = cu_seqlens.shape[0] - 1
-    H, dk = q.shape[-2:]
-    _, S_t = chunk_fwd(q, k, v, g, beta, cu_seqlens=cu_seqlens)
-    eye = torch.eye(dk, dtype=torch.float32, device=q.device).expand(P, H, dk, dk).contiguous()
-    _, M = chunk_fwd(q, k, torch.zeros_like(k), g, beta, initial_state=eye,
-                     cu_seqlens=cu_seqlens)
+    H, dk = k.shape[-2:]
+    _, S_t = chunk_fwd(None, k, v, g, beta, cu_seqlens=cu_seqlens, output=False)
+    eye = torch.eye(dk, dtype=torch.float32, device=k.device).expand(P, H, dk, dk).contiguous()
+    _, M = chunk_fwd(None, k, None, g, beta, initial_state=eye, cu_seqlens=cu_seqlens,
+                     output=False)
     return M, S_t
 
 

@@ -48,7 +48,7 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
                          const float *beta, const float *s0, const int32_t *cu,
                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
                          int32_t d_v, int32_t chunk, kda_dtype dt, const void *o,
-                         const float *sf, const void *ws, size_t ws_bytes)
+                         const float *sf, const void *ws, size_t ws_bytes, bool optional_io)
 {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || total_tokens < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
@@ -61,7 +61,16 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
     // the kernel forms row offsets as 24-bit products: one token's fp32 g row
     // (H d_k 4 bytes) must stay below 2^24 bytes
     if ((int64_t)H * d_k * 4 >= ((int64_t)1 << 24)) return KDA_ERR_SHAPE;
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (total_tokens > 0) {
+        if (!k || !g || !beta) return KDA_ERR_NULL;
+        if (optional_io) {
+            // o may be NULL when the final state is wanted (q is then unused); v
+            // may be NULL for zero values
+            if (o ? !q : !sf) return KDA_ERR_NULL;
+        } else if (!q || !v || !o) {
+            return KDA_ERR_NULL;
+        }
+    }
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
         misaligned(s0) || misaligned(cu) || misaligned(o) || misaligned(sf) || misaligned(ws))
         return KDA_ERR_ALIGN;
@@ -90,7 +99,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
 {
     const kda_status st =
         prefill_check(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, H,
-                      d_k, d_v, chunk_size, dtype, o, final_state, workspace, workspace_bytes);
+                      d_k, d_v, chunk_size, dtype, o, final_state, workspace, workspace_bytes, true);
     if (st != KDA_OK) return st;
     if (num_seqs == 0) return KDA_OK;
     const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
@@ -112,7 +121,7 @@ kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void 
     const kda_status st =
         prefill_check(q_raw, k_raw, v, reinterpret_cast<const float *>(z), beta, initial_state,
                       cu_seqlens, num_seqs, total_tokens, H, d_k, d_v, chunk_size, dtype, o,
-                      final_state, workspace, workspace_bytes);
+                      final_state, workspace, workspace_bytes, false);
     if (st != KDA_OK) return st;
     if (total_tokens > 0 && (!A_log || !b_alpha)) return KDA_ERR_NULL;
     if (misaligned(A_log) || misaligned(b_alpha)) return KDA_ERR_ALIGN;

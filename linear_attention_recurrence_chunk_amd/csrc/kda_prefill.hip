@@ -157,7 +157,8 @@ __device__ __forceinline__ V load_at(const E *base, uint32_t byte_off)
 // the next chunk's loads can be spread over the phases of the current one.
 enum { LOAD_G = 1, LOAD_KQ = 2, LOAD_VB = 4, LOAD_ALL = 7 };
 
-template <bool FUSED, typename T, int DK, int BV>
+// OUT = false (state only): q is not read.  v == nullptr: the values are zero.
+template <bool FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, const SeqView &sv,
                                            int64_t t0, const T *__restrict__ q,
                                            const T *__restrict__ k, const T *__restrict__ v,
@@ -187,18 +188,23 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
             if (parts & LOAD_KQ) {
                 const uint32_t bo = row_byte_off<T>(row, last, rsT, 2 * cp);
                 R.k[r] = load_at<V2>(kb, bo);
-                R.q[r] = load_at<V2>(qb, bo);
+                if (OUT) R.q[r] = load_at<V2>(qb, bo);
             }
         }
     }
     if (parts & LOAD_VB) {
-        const T *vb = v + (t0 * sv.H + sv.head) * DV + sv.v0;
+        if (v) {
+            const T *vb = v + (t0 * sv.H + sv.head) * DV + sv.v0;
 #pragma unroll
-        for (int m = 0; m < Cf::NVV; ++m) {
-            const int vi = t + Cf::NT * m;
-            const int row = min(vi / Cf::VPR, Cf::C - 1), cv = vi % Cf::VPR;
-            R.v[m] = load_at<V8>(vb, row_byte_off<T>(row, last, (uint32_t)(sv.H * DV * sizeof(T)),
-                                                      cv * Cf::VEC));
+            for (int m = 0; m < Cf::NVV; ++m) {
+                const int vi = t + Cf::NT * m;
+                const int row = min(vi / Cf::VPR, Cf::C - 1), cv = vi % Cf::VPR;
+                R.v[m] = load_at<V8>(vb, row_byte_off<T>(row, last, (uint32_t)(sv.H * DV * sizeof(T)),
+                                                          cv * Cf::VEC));
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < Cf::NVV; ++m) R.v[m] = V8{};
         }
         const float *bb = beta + t0 * sv.H + sv.head;
         R.beta = load_at<float>(bb, row_byte_off<float>(t < Cf::C ? t : 0, last, (uint32_t)sv.H * 4u, 0));
@@ -278,7 +284,7 @@ __device__ __forceinline__ float bounded_alpha(float z, float eA, float b)
 // chunk lies in the sequence.  FUSED: g comes from decay logits through the
 // bounded gate, and k and q are divided by their row norms (L2Norm of the
 // function table), whose partial sums of squares are in sm.nrm.
-template <bool FULL, bool FUSED, typename T, int DK, int BV>
+template <bool FULL, bool FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
                                         const GateCtx &gc, int buf)
 {
@@ -346,7 +352,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 kk[cc] = in ? to_f32(R.k[r][cc]) : 0.f;
-                qq[cc] = in ? to_f32(R.q[r][cc]) : 0.f;
+                qq[cc] = (OUT && in) ? to_f32(R.q[r][cc]) : 0.f;
                 if (FUSED) {
                     kk[cc] *= ik;
                     qq[cc] *= iq;
@@ -356,8 +362,9 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
             }
             *reinterpret_cast<V2 *>(&sm.Kr[r0 + r][2 * cp]) =
                 pack2<T>(kk[0] * eL[0][r], kk[1] * eL[1][r]);
-            *reinterpret_cast<V2 *>(&sm.Qr[r0 + r][2 * cp]) =
-                pack2<T>(qq[0] * eL[0][r], qq[1] * eL[1][r]);
+            if (OUT)
+                *reinterpret_cast<V2 *>(&sm.Qr[r0 + r][2 * cp]) =
+                    pack2<T>(qq[0] * eL[0][r], qq[1] * eL[1][r]);
             *reinterpret_cast<V2 *>(&sm.Kc[buf][r0 + r][2 * cp]) = pack2<T>(kc[0], kc[1]);
             *reinterpret_cast<V2 *>(&sm.Kd[r0 + r][2 * cp]) = pack2<T>(kd[0], kd[1]);
         }
@@ -373,12 +380,12 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
     }
 }
 
-template <bool FUSED, typename T, int DK, int BV>
+template <bool FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
                                         const GateCtx &gc, int buf)
 {
-    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED>(sm, R, nv, gc, buf);
-    else e_phase<false, FUSED>(sm, R, nv, gc, buf);
+    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED, OUT>(sm, R, nv, gc, buf);
+    else e_phase<false, FUSED, OUT>(sm, R, nv, gc, buf);
 }
 
 // Sum over the 16 lanes of a row of the wave (lanes 16 j .. 16 j + 15), with
@@ -423,7 +430,7 @@ __device__ __forceinline__ void norm_partials(Smem<T, DK, BV> &sm, const ChunkRe
 // block I by prod_{J<m<I} e^{B_m} (nothing for adjacent blocks), once for
 // both products.  The products are taken transposed so that each lane ends
 // with four consecutive columns of one row.
-template <int I, int J, typename T, int DK, int BV>
+template <int I, int J, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp, int buf)
 {
     typedef Path<T> PT;
@@ -450,7 +457,7 @@ __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp, i
             col = PT::pack(x);
         }
         accA = PT::mma(col, load_frag<T>(&sm.Kr[16 * I + n16][kc]), accA);
-        accP = PT::mma(col, load_frag<T>(&sm.Qr[16 * I + n16][kc]), accP);
+        if (OUT) accP = PT::mma(col, load_frag<T>(&sm.Qr[16 * I + n16][kc]), accP);
     }
     // lane holds X[r][j], r = 16 I + n16, j = 16 J + 4 grp + i
     const int r = 16 * I + n16;
@@ -462,7 +469,7 @@ __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp, i
         wp[i] = accP[i];
     }
     *reinterpret_cast<V4 *>(&sm.An[r][16 * J + 4 * grp]) = pack4<T>(wa);
-    *reinterpret_cast<V4 *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(wp);
+    if (OUT) *reinterpret_cast<V4 *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(wp);
 }
 
 // Decay tables of the chunk for channel c: e^{E_J} = prod_{m<J} e^{B_m}
@@ -520,7 +527,7 @@ __device__ __forceinline__ float load_frag_tr(const float *x, int ld, int k0, in
 // back in the D layout (rows of the block in 4 grp + i, value columns in n16);
 // Z transposed (value columns in 4 grp + i, rows in n16), as the output's
 // transposed product needs it.
-template <bool SCALE, int NV, typename T, int DK, int BV>
+template <bool SCALE, int NV, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, int n16, int grp,
                                          f32x4 (&Y)[NV], f32x4 (&Zt)[NV])
 {
@@ -532,7 +539,8 @@ __device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, in
         float f[KPL];
         if (SCALE) load_f32<KPL>(f, &sm.eE[I][kc]);
         const typename PT::frag kr = load_frag<T>(&sm.Kr[16 * I + n16][kc]);
-        const typename PT::frag qr = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
+        typename PT::frag qr{};
+        if (OUT) qr = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             typename PT::frag s = load_frag<T>(&sm.ST[16 * (vt0 + v) + n16][kc]);
@@ -544,14 +552,14 @@ __device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, in
                 s = PT::pack(x);
             }
             Y[v] = PT::mma(kr, s, Y[v]);
-            Zt[v] = PT::mma(s, qr, Zt[v]);
+            if (OUT) Zt[v] = PT::mma(s, qr, Zt[v]);
         }
     }
 }
 
 // State read-out of job (I, value tiles vt0 .. vt0 + NV - 1): Y and Z^T by
 // yz_block, then R = B (V - Y) stored transposed for the substitution.
-template <bool SCALE, int NV, typename T, int DK, int BV>
+template <bool SCALE, int NV, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void readout_r(Smem<T, DK, BV> &sm, int I, int vt0, f32x4 (&Zt)[NV])
 {
     typedef typename Vec<T>::four V4;
@@ -559,7 +567,7 @@ __device__ __forceinline__ void readout_r(Smem<T, DK, BV> &sm, int I, int vt0, f
     f32x4 Y[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) Y[v] = zero4();
-    yz_block<SCALE, NV>(sm, I, vt0, n16, grp, Y, Zt);
+    yz_block<SCALE, NV, OUT>(sm, I, vt0, n16, grp, Y, Zt);
     const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * I + 4 * grp]);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -580,8 +588,10 @@ __device__ __forceinline__ int rows_in(int64_t t0, int64_t eos, int C)
 }
 
 // FUSED: q and k arrive unnormalised and g is replaced by decay logits z with
-// the per-head gate parameters A_log [H] and b_alpha [H][DK].
-template <typename T, int DK, int BV, int DV, bool FUSED>
+// the per-head gate parameters A_log [H] and b_alpha [H][DK].  OUT = false:
+// only the final state is computed (no o, q not read, and neither P nor
+// (Q o e^G) S is formed); v == nullptr stands for zero values.
+template <typename T, int DK, int BV, int DV, bool FUSED, bool OUT>
 __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
@@ -653,9 +663,11 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         }
     }
     // constant zero blocks above the diagonal of P
-    for (int e = t; e < C * C; e += NT) {
-        const int r = e / C, j = e % C;
-        if ((j >> 4) > (r >> 4)) sm.P[r][j] = from_f32<T>(0.f);
+    if (OUT) {
+        for (int e = t; e < C * C; e += NT) {
+            const int r = e / C, j = e % C;
+            if ((j >> 4) > (r >> 4)) sm.P[r][j] = from_f32<T>(0.f);
+        }
     }
 
     // (row block, pair of value tiles) job of this wave for the state read-out
@@ -681,12 +693,12 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const int64_t nchunks = (sv.eos - sv.bos + C - 1) / C;
     ChunkRegs<T, DK, BV> R;
     if (nchunks > 0) {
-        load_chunk<FUSED>(R, LOAD_ALL, sv, sv.bos, q, k, v, g, z, beta, DV);
+        load_chunk<FUSED, OUT>(R, LOAD_ALL, sv, sv.bos, q, k, v, g, z, beta, DV);
         if (FUSED) {
             norm_partials(sm, R);
             __syncthreads();
         }
-        e_phase<FUSED>(sm, R, rows_in(sv.bos, sv.eos, C), gc, 0);
+        e_phase<FUSED, OUT>(sm, R, rows_in(sv.bos, sv.eos, C), gc, 0);
     }
     __syncthreads();
 
@@ -697,7 +709,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         const int nv = rows_in(t0, sv.eos, C);           // rows of this chunk in the sequence
         const bool more = ch + 1 < nchunks;
         const int kbuf = (int)(ch & 1);                  // Kc buffer of this chunk
-        if (more) load_chunk<FUSED>(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, z, beta, DV);
+        if (more) load_chunk<FUSED, OUT>(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, z, beta, DV);
 
         // ================= AP
         if (wv < NB) {
@@ -710,10 +722,12 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 const int kc = ks * KS + grp * KPL;
                 const typename PT::frag fd = load_frag<T>(&sm.Kd[16 * I + n16][kc]);
                 const typename PT::frag fk = load_frag<T>(&sm.Kr[16 * I + n16][kc]);
-                const typename PT::frag fq = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
                 accAt = PT::mma(fd, fk, accAt);   // [r = n16][j = 4 grp + i]
                 accA = PT::mma(fk, fd, accA);     // [r = 4 grp + i][j = n16]
-                accPt = PT::mma(fd, fq, accPt);   // [r = n16][j = 4 grp + i]
+                if (OUT) {
+                    const typename PT::frag fq = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
+                    accPt = PT::mma(fd, fq, accPt);   // [r = n16][j = 4 grp + i]
+                }
             }
             // N = A_II in the A-operand layout (Na: N[n16][4 grp + i]) and in the
             // D layout (Nd: N[4 grp + i][n16])
@@ -727,7 +741,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 Nd[i] = n16 < jl ? b4[i] * accA[i] : 0.f;
                 pv[i] = jl <= n16 ? accPt[i] : 0.f;
             }
-            *reinterpret_cast<V4 *>(&sm.P[16 * I + n16][16 * I + 4 * grp]) = pack4<T>(pv);
+            if (OUT) *reinterpret_cast<V4 *>(&sm.P[16 * I + n16][16 * I + 4 * grp]) = pack4<T>(pv);
             // A lane's values of X in the A layout are those of X^T in the D
             // layout.  So mma16(Xd, Xa), which multiplies X^T by X^T, returns
             // (X^2)^T in the D layout, i.e. X^2 in the A layout: every power of
@@ -756,12 +770,12 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             // that the four SIMDs get similar shares
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
             switch (wv - NB) {
-                case 0: ap_pair<3, 0>(sm, n16, grp, kbuf); break;
-                case 1: ap_pair<2, 0>(sm, n16, grp, kbuf); break;
-                case 2: ap_pair<3, 1>(sm, n16, grp, kbuf); break;
-                case 3: ap_pair<1, 0>(sm, n16, grp, kbuf); break;
-                case 4: ap_pair<2, 1>(sm, n16, grp, kbuf); break;
-                default: ap_pair<3, 2>(sm, n16, grp, kbuf); break;
+                case 0: ap_pair<3, 0, OUT>(sm, n16, grp, kbuf); break;
+                case 1: ap_pair<2, 0, OUT>(sm, n16, grp, kbuf); break;
+                case 2: ap_pair<3, 1, OUT>(sm, n16, grp, kbuf); break;
+                case 3: ap_pair<1, 0, OUT>(sm, n16, grp, kbuf); break;
+                case 4: ap_pair<2, 1, OUT>(sm, n16, grp, kbuf); break;
+                default: ap_pair<3, 2, OUT>(sm, n16, grp, kbuf); break;
             }
         } else if (wv >= Cf::NW - 2) {
             // decay tables, one channel per thread
@@ -769,15 +783,15 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             if (c < DK) decay_tables(sm, c);
         }
         __syncthreads();   // ---------------------------------------------- B1
-        if (more) load_chunk<FUSED>(R, LOAD_VB, sv, t0 + C, q, k, v, g, z, beta, DV);
+        if (more) load_chunk<FUSED, OUT>(R, LOAD_VB, sv, t0 + C, q, k, v, g, z, beta, DV);
 
         // ================= YZ: state read-out for row blocks 1.. and R = B (V - Y)
         if (has_job) {
             f32x4 (&Zt)[2] = *reinterpret_cast<f32x4 (*)[2]>(&W[0]);
             Zt[0] = zero4();
             Zt[1] = zero4();
-            if (jI > 0) readout_r<true, 2>(sm, jI, jvt, Zt);
-            else readout_r<false, 2>(sm, 0, jvt, Zt);
+            if (jI > 0) readout_r<true, 2, OUT>(sm, jI, jvt, Zt);
+            else readout_r<false, 2, OUT>(sm, 0, jvt, Zt);
         }
         // fused prologue: the next chunk's row norms, read by its E after B2
         if (FUSED && more) norm_partials(sm, R);
@@ -809,7 +823,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         }
         // ================= the next chunk's elementwise phase (the substituting
         // waves do their share after their substitution)
-        if (more) e_phase<FUSED>(sm, R, rows_in(t0 + C, sv.eos, C), gc, kbuf ^ 1);
+        if (more) e_phase<FUSED, OUT>(sm, R, rows_in(t0 + C, sv.eos, C), gc, kbuf ^ 1);
         __syncthreads();   // ---------------------------------------------- B3
 
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
@@ -845,7 +859,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 *reinterpret_cast<V4 *>(&sm.ST[16 * vt + n16][16 * ct + 4 * grp]) = pack4<T>(s4);
             }
         }
-        if (has_job) {
+        if (OUT && has_job) {
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
             // transposed blocks: lane holds O[16 jI + n16][16 (jvt + v) + 4 grp + i]
             const int nks = (16 * (jI + 1) + KS - 1) / KS;
@@ -883,7 +897,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     }
 }
 
-template <typename T, int D, int BV, bool FUSED>
+template <typename T, int D, int BV, bool FUSED, bool OUT>
 static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *s0, const int32_t *cu,
                                    int num_seqs, int64_t seq_len, int H, void *o, float *sf,
@@ -894,14 +908,14 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
     if (nwork == 0) return hipSuccess;
     // token row strides in bytes (fp32 g is the widest) must fit 24 bits
     if ((int64_t)H * D * 4 >= (int64_t)1 << 24) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FUSED>), dim3((unsigned)nwork),
+    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FUSED, OUT>), dim3((unsigned)nwork),
                        dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)q, (const T *)k,
                        (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (T *)o, sf,
                        (const T *)z, A_log, b_alpha);
     return hipGetLastError();
 }
 
-template <bool FUSED>
+template <bool FUSED, bool OUT>
 static hipError_t launch_prefill_f(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *s0, const int32_t *cu,
                                    int num_seqs, int64_t seq_len, int H, int d, bool is_bf16,
@@ -911,14 +925,14 @@ static hipError_t launch_prefill_f(const void *q, const void *k, const void *v, 
 #define KDA_PREFILL_ARGS q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, o, sf, z, A_log, b_alpha, stream
     if (is_bf16) {
         switch (d) {
-            case 32: return launch_prefill_t<bf16, 32, 32, FUSED>(KDA_PREFILL_ARGS);
-            case 64: return launch_prefill_t<bf16, 64, 64, FUSED>(KDA_PREFILL_ARGS);
-            case 128: return launch_prefill_t<bf16, 128, 64, FUSED>(KDA_PREFILL_ARGS);
+            case 32: return launch_prefill_t<bf16, 32, 32, FUSED, OUT>(KDA_PREFILL_ARGS);
+            case 64: return launch_prefill_t<bf16, 64, 64, FUSED, OUT>(KDA_PREFILL_ARGS);
+            case 128: return launch_prefill_t<bf16, 128, 64, FUSED, OUT>(KDA_PREFILL_ARGS);
         }
     } else {
         switch (d) {
-            case 32: return launch_prefill_t<float, 32, 32, FUSED>(KDA_PREFILL_ARGS);
-            case 64: return launch_prefill_t<float, 64, 32, FUSED>(KDA_PREFILL_ARGS);
+            case 32: return launch_prefill_t<float, 32, 32, FUSED, OUT>(KDA_PREFILL_ARGS);
+            case 64: return launch_prefill_t<float, 64, 32, FUSED, OUT>(KDA_PREFILL_ARGS);
         }
     }
 #undef KDA_PREFILL_ARGS
@@ -931,8 +945,11 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, const flo
                           float *sf, hipStream_t stream)
 {
     if (chunk != 64) return hipErrorInvalidValue;
-    return launch_prefill_f<false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d, is_bf16, o,
-                                   sf, nullptr, nullptr, nullptr, stream);
+    if (!o)   // state only
+        return launch_prefill_f<false, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
+                                              is_bf16, o, sf, nullptr, nullptr, nullptr, stream);
+    return launch_prefill_f<false, true>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d, is_bf16,
+                                         o, sf, nullptr, nullptr, nullptr, stream);
 }
 
 hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
@@ -942,8 +959,9 @@ hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void
                                 bool is_bf16, void *o, float *sf, hipStream_t stream)
 {
     if (chunk != 64) return hipErrorInvalidValue;
-    return launch_prefill_f<true>(q_raw, k_raw, v, nullptr, beta, s0, cu, num_seqs, seq_len, H, d,
-                                  is_bf16, o, sf, z, A_log, b_alpha, stream);
+    if (!o) return hipErrorInvalidValue;
+    return launch_prefill_f<true, true>(q_raw, k_raw, v, nullptr, beta, s0, cu, num_seqs, seq_len, H,
+                                        d, is_bf16, o, sf, z, A_log, b_alpha, stream);
 }
 
 }  // namespace kda

@@ -77,8 +77,10 @@ def _dec(**kw):
 
 @gpu_visible
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), ENULL), (dict(k=None), ENULL), (dict(v=None), ENULL), (dict(g=None), ENULL),
-    (dict(beta=None), ENULL), (dict(o=None), ENULL),
+    (dict(q=None), ENULL), (dict(k=None), ENULL), (dict(g=None), ENULL),
+    (dict(beta=None), ENULL),
+    (dict(o=None), ENULL),                           # no output and no final state
+    (dict(o=None, q=None), ENULL),                   # likewise (v = NULL alone is valid: zero values)
     (dict(total=-1), ESHAPE), (dict(num_seqs=-1), ESHAPE), (dict(H=0), ESHAPE),
     (dict(num_seqs=3, total=128), ESHAPE),           # equal lengths need a multiple
     (dict(num_seqs=0, total=5), ESHAPE),

@@ -276,3 +276,33 @@ def test_prefill_many_heads():
     eo, es = run_prefill(x, 64, heads=[0, 97, 255])
     report("prefill H=256", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# state-only calls (o = NULL) and zero values (v = NULL)
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.float32, 32), (torch.float32, 64)])
+def test_prefill_state_only(dtype, d):
+    w = inputs.custom(H=3, dk=d, dv=d, seqlens=[100, 0, 64, 1, 200], state_std=0.1, dtype=dtype)
+    x = inputs.prefill_inputs(w, seed=60 + d, device=DEV)
+    args = (x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
+    _, sf_full = kda.chunk_fwd(x["q"], *args)
+    o_none, sf = kda.chunk_fwd(None, *args, output=False)
+    torch.cuda.synchronize()
+    assert o_none is None
+    # the state path is the same arithmetic with or without the output
+    es_full = rel_err(sf, sf_full.cpu().double().numpy())
+    # zero values: the oracle with v = 0
+    _, sz = kda.chunk_fwd(None, x["k"], None, x["g"], x["beta"], x["initial_state"],
+                          x["cu_seqlens"], output=False)
+    torch.cuda.synchronize()
+    cpu = lambda t: t.cpu()
+    _, sz_ref = oracle.forward(cpu(x["q"]), cpu(x["k"]), torch.zeros_like(cpu(x["v"])),
+                               cpu(x["g"]), cpu(x["beta"]), cpu(x["initial_state"]),
+                               x["cu_seqlens"].cpu().numpy())
+    _, sf_ref = oracle.forward(cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), cpu(x["g"]),
+                               cpu(x["beta"]), cpu(x["initial_state"]),
+                               x["cu_seqlens"].cpu().numpy())
+    es, ez = rel_err(sf, sf_ref), rel_err(sz, sz_ref)
+    report(f"prefill state only {dtype} d={d}", vs_full=es_full, state=es, zero_v=ez)
+    assert es_full <= 1e-6 and es <= TOL[dtype] and ez <= TOL[dtype]
