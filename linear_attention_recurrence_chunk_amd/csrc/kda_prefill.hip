@@ -609,17 +609,16 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     __shared__ __align__(16) Sm sm;
 
     // ---- work item w = NSLICE (sequence H + head) + slice.  Workgroups are
-    // dealt to the 8 XCDs round-robin (block b to XCD b mod 8).  When the count
-    // allows, the slices of one head go to blocks of one residue mod 8, so that
-    // they share q, k, g through that XCD's L2, and consecutive heads go to
-    // consecutive XCDs, so that every XCD gets a share of every sequence
+    // dealt to the 8 XCDs round-robin (block b to XCD b mod 8).  When H divides
+    // by 8, XCD x takes heads [x H/8, (x + 1) H/8) of every sequence in turn:
+    // the slices of a head share q, k, g through one L2, an XCD reads
+    // contiguous row segments, and every XCD gets a share of every sequence
     // whatever the mix of sequence lengths.
-    const int64_t nwork = (int64_t)num_seqs * H * NSLICE;
     const int64_t b = blockIdx.x;
     int64_t w = b;
-    if (nwork % (8 * NSLICE) == 0) {
-        const int64_t q8 = b / (8 * NSLICE), r8 = b % (8 * NSLICE);
-        w = NSLICE * (8 * q8 + r8 % 8) + r8 / 8;
+    if (H % 8 == 0) {
+        const int64_t x = b % 8, slot = b / 8, per_seq = (int64_t)(H / 8) * NSLICE;
+        w = ((slot / per_seq) * H + x * (H / 8)) * NSLICE + slot % per_seq;
     }
     const int seq = (int)(w / ((int64_t)H * NSLICE));
     const int head = (int)((w / NSLICE) % H);
