@@ -43,7 +43,8 @@
 //   YZ   one wave per (row block I, pair of value tiles): (K o e^G) S and
 //        (Q o e^G) S for its 16 rows and 32 value columns, then
 //        R = B (V - (K o e^G) S).
-//   U    one wave per 16 value columns: the forward substitution.
+//   U    one wave per 16 value columns: the forward substitution (for d <= 64
+//        on waves that have no elementwise work).
 //   SO   the read-out waves: their two blocks of O = (Q o e^G) S + P U,
 //        stored to o; waves 8 ..: one state row tile each, S' = Diag(gamma) S +
 //        Kbar^T U, the state staying in their registers across chunks.  Kbar^T
@@ -797,11 +798,13 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         __syncthreads();   // ---------------------------------------------- B2
 
         // ================= U: forward substitution, one wave per value tile;
-        // U^T overwrites R^T in place
-        if (wv < NVT) {
+        // U^T overwrites R^T in place.  On waves the elementwise phase leaves
+        // free when there are enough (d <= 64), else on waves 0 ..
+        constexpr int UW0 = Cf::EWAVES + NVT <= Cf::NW ? Cf::EWAVES : 0;
+        if (wv >= UW0 && wv < UW0 + NVT) {
             typedef typename PT::quad Q4;
             const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
-            const int vt = wv;
+            const int vt = wv - UW0;
             Q4 Ub[NB];
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
