@@ -530,7 +530,7 @@ __device__ __forceinline__ float load_frag_tr(const float *x, int ld, int k0, in
 // transposed product needs it.
 template <bool SCALE, int NV, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, int n16, int grp,
-                                         f32x4 (&Y)[NV], f32x4 (&Zt)[NV])
+                                         f32x4 (&Y)[NV], f32x4 *Zt)
 {
     typedef Path<T> PT;
     constexpr int KS = PT::KS, KPL = PT::KPL;
@@ -561,7 +561,7 @@ __device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, in
 // State read-out of job (I, value tiles vt0 .. vt0 + NV - 1): Y and Z^T by
 // yz_block, then R = B (V - Y) stored transposed for the substitution.
 template <bool SCALE, int NV, bool OUT, typename T, int DK, int BV>
-__device__ __forceinline__ void readout_r(Smem<T, DK, BV> &sm, int I, int vt0, f32x4 (&Zt)[NV])
+__device__ __forceinline__ void readout_r(Smem<T, DK, BV> &sm, int I, int vt0, f32x4 *Zt)
 {
     typedef typename Vec<T>::four V4;
     const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
@@ -787,11 +787,10 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
 
         // ================= YZ: state read-out for row blocks 1.. and R = B (V - Y)
         if (has_job) {
-            f32x4 (&Zt)[2] = *reinterpret_cast<f32x4 (*)[2]>(&W[0]);
-            Zt[0] = zero4();
-            Zt[1] = zero4();
-            if (jI > 0) readout_r<true, 2, OUT>(sm, jI, jvt, Zt);
-            else readout_r<false, 2, OUT>(sm, 0, jvt, Zt);
+            W[0] = zero4();   // Z^T of the two blocks accumulates in W[0], W[1]
+            W[1] = zero4();
+            if (jI > 0) readout_r<true, 2, OUT>(sm, jI, jvt, W);
+            else readout_r<false, 2, OUT>(sm, 0, jvt, W);
         }
         // fused prologue: the next chunk's row norms, read by its E after B2
         if (FUSED && more) norm_partials(sm, R);
