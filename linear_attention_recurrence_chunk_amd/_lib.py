@@ -90,6 +90,23 @@ def _need(x, name, dtype=None, ndim=None, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _gpu(dev: torch.device):
+    """The kernels take device pointers: refuse tensors that are not on a GPU."""
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {dev}")
+
+
+def _out(out: Optional[torch.Tensor], shape, dtype, dev, name: str = "out") -> torch.Tensor:
+    """A new output tensor, or the caller's after checking it matches exactly
+    (the kernels write every element of the expected shape)."""
+    if out is None:
+        return torch.empty(tuple(shape), dtype=dtype, device=dev)
+    _need(out, name, dtype=dtype, device=dev)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    return out
+
+
 def workspace_size(num_seqs: int, total_tokens: int, H: int, d: int, chunk_size: int,
                    dtype: torch.dtype) -> int:
     return int(library().kda_chunk_fwd_workspace_size(num_seqs, total_tokens, H, d, d,
@@ -120,6 +137,7 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
     if k.dtype not in _DTYPES:
         raise ValueError(f"k must be bf16 or fp32, got {k.dtype}")
     dev = k.device
+    _gpu(dev)
     _need(k, "k", ndim=(3, 4))
     if q is not None:
         _need(q, "q", dtype=k.dtype, ndim=(k.dim(),), device=dev)
@@ -151,16 +169,9 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
         _need(initial_state, "initial_state", dtype=torch.float32, device=dev)
         if tuple(initial_state.shape) != sshape:
             raise ValueError(f"initial_state must have shape {sshape}")
-    if not output:
-        out = None
-    elif out is None:
-        out = torch.empty(k.shape[:-1] + (dv,), dtype=k.dtype, device=dev)
-    else:
-        _need(out, "out", dtype=k.dtype, device=dev)
-    if final_state is None and output_final_state:
-        final_state = torch.empty(sshape, dtype=torch.float32, device=dev)
-    elif final_state is not None:
-        _need(final_state, "final_state", dtype=torch.float32, device=dev)
+    out = _out(out, k.shape[:-1] + (dv,), k.dtype, dev) if output else None
+    if final_state is not None or output_final_state:
+        final_state = _out(final_state, sshape, torch.float32, dev, "final_state")
     ws_bytes = workspace_size(num_seqs, n_tok, H, dk, chunk_size, k.dtype)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     lib = library()
@@ -180,6 +191,7 @@ def step_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     if q.dtype not in _DTYPES:
         raise ValueError(f"q must be bf16 or fp32, got {q.dtype}")
     dev = q.device
+    _gpu(dev)
     _need(q, "q", ndim=(3,))
     _need(k, "k", dtype=q.dtype, ndim=(3,), device=dev)
     _need(v, "v", dtype=q.dtype, ndim=(3,), device=dev)
@@ -192,8 +204,7 @@ def step_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
         raise ValueError("q, k, g must share a shape and v must match it up to d_v")
     if tuple(beta.shape) != (N, H) or tuple(state.shape) != (N, H, dk, dv):
         raise ValueError("beta must be [N, H] and state [N, H, d_k, d_v]")
-    if out is None:
-        out = torch.empty_like(v)
+    out = _out(out, v.shape, v.dtype, dev)
     st = library().kda_step_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                    _ptr(out), N, H, dk, dv, _DTYPES[q.dtype], _stream(dev))
     _check("kda_step_decode", st)
@@ -225,6 +236,7 @@ def chunk_fwd_fused(q_raw: torch.Tensor, k_raw: torch.Tensor, v: torch.Tensor, z
     if q_raw.dtype not in _DTYPES:
         raise ValueError(f"q_raw must be bf16 or fp32, got {q_raw.dtype}")
     dev = q_raw.device
+    _gpu(dev)
     _need(q_raw, "q_raw", ndim=(3, 4))
     for name, x in (("k_raw", k_raw), ("v", v), ("z", z)):
         _need(x, name, dtype=q_raw.dtype, ndim=(q_raw.dim(),), device=dev)
@@ -261,14 +273,14 @@ def output_gate(o_raw: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor,
     if o_raw.dtype not in _DTYPES:
         raise ValueError(f"o_raw must be bf16 or fp32, got {o_raw.dtype}")
     dev = o_raw.device
+    _gpu(dev)
     _need(o_raw, "o_raw")
     _need(gate, "gate", dtype=o_raw.dtype, device=dev)
     _need(weight, "weight", dtype=torch.float32, ndim=(1,), device=dev)
     dv = o_raw.shape[-1]
     if gate.shape != o_raw.shape or tuple(weight.shape) != (dv,):
         raise ValueError("gate must match o_raw and weight must be [d_v]")
-    if out is None:
-        out = torch.empty_like(o_raw)
+    out = _out(out, o_raw.shape, o_raw.dtype, dev)
     st = library().kda_output_gate(_ptr(o_raw), _ptr(gate), _ptr(weight), float(eps), _ptr(out),
                                    o_raw.numel() // dv, dv, _DTYPES[o_raw.dtype], _stream(dev))
     _check("kda_output_gate", st)
@@ -284,6 +296,7 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: Optional[torch
     if x.dtype not in _DTYPES:
         raise ValueError(f"x must be bf16 or fp32, got {x.dtype}")
     dev = x.device
+    _gpu(dev)
     _need(x, "x", ndim=(2,))
     _need(weight, "weight", dtype=torch.float32, ndim=(2,), device=dev)
     n_tok, C = x.shape
@@ -309,14 +322,14 @@ def state_compose(M: torch.Tensor, S_in: torch.Tensor, S_tilde: torch.Tensor,
                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """S_out = M @ S_in + S_tilde over a batch of fp32 matrices (kda_state_compose)."""
     dev = M.device
+    _gpu(dev)
     for name, x in (("M", M), ("S_in", S_in), ("S_tilde", S_tilde)):
         _need(x, name, dtype=torch.float32, device=dev)
     d = M.shape[-1]
     if M.shape[-2] != d or S_in.shape != S_tilde.shape or S_in.shape[:-2] != M.shape[:-2] \
             or S_in.shape[-2] != d:
         raise ValueError("M must be [..., d, d] and S_in, S_tilde [..., d, d_v]")
-    if out is None:
-        out = torch.empty_like(S_in)
+    out = _out(out, S_in.shape, torch.float32, dev)
     count = M.numel() // (d * d)
     st = library().kda_state_compose(_ptr(M), _ptr(S_in), _ptr(S_tilde), _ptr(out), count, d,
                                      S_in.shape[-1], _stream(dev))

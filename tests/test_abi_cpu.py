@@ -127,6 +127,13 @@ def test_python_binding_validates_before_the_call():
         _lib.chunk_fwd(q, q, q, q, torch.zeros(8, 3))
     with pytest.raises(ValueError):
         _lib.step_decode(q, q, q, q, torch.zeros(8, 2), torch.zeros(8, 2, 32, 16))
+    # well-formed tensors in host memory are refused: the kernels take device pointers
+    with pytest.raises(ValueError, match="GPU device"):
+        _lib.chunk_fwd(q, q, q, q, torch.zeros(8, 2))
+    with pytest.raises(ValueError, match="GPU device"):
+        _lib.step_decode(q, q, q, q, torch.zeros(8, 2), torch.zeros(8, 2, 32, 32))
+    with pytest.raises(ValueError, match="GPU device"):
+        _lib.output_gate(q, q, torch.ones(32))
 
 
 def _fused(**kw):

@@ -306,3 +306,22 @@ def test_prefill_state_only(dtype, d):
     es, ez = rel_err(sf, sf_ref), rel_err(sz, sz_ref)
     report(f"prefill state only {dtype} d={d}", vs_full=es_full, state=es, zero_v=ez)
     assert es_full <= 1e-6 and es <= TOL[dtype] and ez <= TOL[dtype]
+
+
+def test_binding_rejects_mismatched_outputs():
+    # preallocated outputs must match exactly: the kernels write every element
+    w = inputs.custom(H=2, dk=32, dv=32, seqlens=[64], dtype=torch.float32)
+    x = inputs.prefill_inputs(w, seed=3, device=DEV)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"])
+    with pytest.raises(ValueError, match="out must have shape"):
+        kda.chunk_fwd(*args, out=torch.empty(63, 2, 32, device=DEV))
+    with pytest.raises(ValueError, match="final_state must have shape"):
+        kda.chunk_fwd(*args, final_state=torch.empty(1, 2, 32, 16, device=DEV))
+    wd = inputs.custom(H=2, dk=32, dv=32, dtype=torch.float32, decode_requests=3)
+    xd = inputs.decode_inputs(wd, seed=3, device=DEV)
+    with pytest.raises(ValueError, match="out must have shape"):
+        kda.step_decode(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["state"],
+                        out=torch.empty(2, 2, 32, device=DEV))
+    M = torch.zeros(4, 32, 32, device=DEV)
+    with pytest.raises(ValueError, match="out must have shape"):
+        kda.state_compose(M, M, M, out=torch.empty(3, 32, 32, device=DEV))
