@@ -9,8 +9,9 @@
 //   - state composition for context-parallel segments: S_out = M S_in + S~
 //     ("Glossaire", entry "KCP"; notation table rows M_t and S~).
 // The first two are elementwise and bound by HBM bandwidth: coalesced accesses
-// (16-byte lanes for the gate, 8-byte for ShortConv), fp32 arithmetic.  The composition is a batch of dense fp32
-// products on the matrix cores (v_mfma_f32_16x16x4_f32).
+// (16-byte lanes for the gate, 8-byte for ShortConv), fp32 arithmetic.  The
+// composition is a batch of dense fp32 products on the matrix cores
+// (v_mfma_f32_16x16x4_f32).
 #include "kda_common.hpp"
 
 namespace kda {
