@@ -23,10 +23,12 @@
 //     U_I = (I + A_II)^-1 (R_I - sum_{J<I} A_IJ U_J),   R = B (V - (K o e^G) S).
 //
 // Decay factors never leave the float range.  With L the sub-block-local
-// inclusive cumulative sum of g and B_J the total log decay of sub-block J:
+// inclusive cumulative sum of g, B_J the total log decay of sub-block J and E_I
+// the log decay from the chunk start to sub-block I:
 //   rows of sub-block I (row operand):   e^{L_r}                     in [e^-80, 1]
-//   columns (stored operand):            e^{-L_j}                    in [1, e^80]
+//   columns of the diagonal blocks:      e^{-L_j}                    in [1, e^80]
 //   column operand of block (I, J < I):  e^{-L_j} prod_{J<=m<I} e^{B_m}   <= 1
+//   state read-out rows (Kg, Qg):        e^{G_r} = e^{E_I} e^{L_r}   <= 1
 // e^80 is the bound the "Glossaire" entry "Decroissance bornee" gives for
 // g_min = -5 (16 tokens times 5; see also the box "Limite importante" of page
 // "Vecteurs, embeddings, espaces de representation").  A factor that
@@ -35,20 +37,24 @@
 //
 // Work split: 16 waves, each with a fixed job in every phase of a chunk.
 //   E    all waves: decays of a (16-token sub-block, channel pair, 4 rows) item
-//        and the operand tiles K o e^L, Q o e^L, K o e^{B-L}, K o e^-L; it runs
-//        in the previous chunk's U phase.
-//   AP   waves 0-3: diagonal block I of A and P and the inverse of I + A_II,
+//        and the operand tiles K o e^L, Q o e^L, K o e^{B-L} and e^{B_I},
+//        e^{-B_I}; it runs in the previous chunk's U phase.
+//   AP   waves 0-3: diagonal block I of A and P (column operand K o e^{-L},
+//        formed from K o e^{B-L} and e^{-B_I}) and the inverse of I + A_II,
 //        kept in registers; waves 4-9: one pair of off-diagonal blocks of A
 //        and P; waves 14-15: the decay tables.
 //   YZ   one wave per (row block I, pair of value tiles): (K o e^G) S and
-//        (Q o e^G) S for its 16 rows and 32 value columns, then
-//        R = B (V - (K o e^G) S).
+//        (Q o e^G) S for its 16 rows and 32 value columns, from the tiles
+//        Kg, Qg built one chunk ahead, then R = B (V - (K o e^G) S); the state
+//        waves take their Kbar^T fragments (K o e^{B-L} through the LDS
+//        transpose read, times the decay to the chunk end) into LDS.
 //   U    one wave per 16 value columns: the forward substitution (for d <= 64
 //        on waves that have no elementwise work).
 //   SO   the read-out waves: their two blocks of O = (Q o e^G) S + P U,
-//        stored to o; waves 8 ..: one state row tile each, S' = Diag(gamma) S +
-//        Kbar^T U, the state staying in their registers across chunks.  Kbar^T
-//        comes from the token-major K o e^{B-L} through the LDS transpose read.
+//        stored to o, then a share of the next chunk's Kg, Qg (diagonal
+//        scalings on the matrix cores); waves 8 ..: one state row tile each,
+//        S' = Diag(gamma) S + Kbar^T U, the state staying in their registers
+//        across chunks.
 // Contractions run on the matrix cores (v_mfma_f32_16x16x32_bf16 and
 // v_mfma_f32_16x16x16_bf16, or v_mfma_f32_16x16x4_f32 for fp32 inputs) with
 // fp32 accumulation; operands are rounded to the input type.  The fp32 state
@@ -92,20 +98,24 @@ struct Smem {
     typedef Cfg<T, DK, BV> Cf;
     T Kr[Cf::C][Cf::LDK];       // K o e^{L}         row operand
     T Qr[Cf::C][Cf::LDK];       // Q o e^{L}
-    T Kc[2][Cf::C][Cf::LDK];    // K o e^{B - L}     column operand, blocks J < I; two
-                                //                   buffers: the state update reads it
-                                //                   after the next chunk's E has run
-    T Kd[Cf::C][Cf::LDK];       // K o e^{-L}        column operand, diagonal blocks
+    T Kc[Cf::C][Cf::LDK];       // K o e^{B - L}     column operand; times e^{-B}, that
+                                //                   of the diagonal blocks
+    T Kg[Cf::C - 16][Cf::LDK];  // K o e^{G}, rows 16 ..: read-out row operand on the
+    T Qg[Cf::C - 16][Cf::LDK];  // Q o e^{G}          chunk-start reference
     T P[Cf::C][Cf::LDC];        // Tril((Q o e^G)(K o e^-G)^T)
-    T An[Cf::C][Cf::LDC];       // -A, blocks J < I
+    T An[Cf::C - 16][Cf::LDC];  // -A, blocks J < I (row r at r - 16: block 0 has none)
     T Tm[Cf::NB][16][Cf::LD16]; // (I + A_II)^-1
     T ST[BV][Cf::LDK];          // state slice, transposed operand copy
     T RT[BV][Cf::LDC];          // R^T, overwritten in place by U^T
     T V[Cf::C][Cf::LDV];        // value slice
     float eB[Cf::NB][DK];       // e^{B_J}
-    float eE[Cf::NB + 1][DK];   // prod_{m<J} e^{B_m}; row NB: whole-chunk decay
+    float eBr[Cf::NB][DK];      // e^{-B_J}
+    float eE[DK];               // whole-chunk decay prod_m e^{B_m}
     float eTx[Cf::NB][DK];      // prod_{m>J} e^{B_m}
     float beta[Cf::C];
+    // (K o e^{G_n - G})^T fragments of the state waves, per (row tile, k step,
+    // lane): built in the read-out phase, used in the state update
+    typename Path<T>::frag KbT[Cf::NCT][Cf::C / Path<T>::KS][64];
     float nrm[2][Cf::C][Cf::WPB];  // fused prologue: partial sums of squares of k, q rows
     float bA[DK];                  // fused prologue: decay bias b_alpha^h of the head
 };
@@ -169,7 +179,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
     typedef Cfg<T, DK, BV> Cf;
     typedef typename Vec<T>::two V2;
     typedef typename Vec<T>::eight_bytes V8;
-    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+    const int t = threadIdx.x, wv = wave_id(), lane = t & 63;
     const int64_t nvalid = sv.eos - t0;                    // >= 1
     const int last = nvalid < Cf::C ? (int)nvalid - 1 : Cf::C - 1;
     const int64_t cbase = (t0 * sv.H + sv.head) * DK;      // wave-uniform
@@ -210,17 +220,6 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, c
         const float *bb = beta + t0 * sv.H + sv.head;
         R.beta = load_at<float>(bb, row_byte_off<float>(t < Cf::C ? t : 0, last, (uint32_t)sv.H * 4u, 0));
     }
-}
-
-// The lane index, hidden from the optimiser.  Taken at the start of each phase
-// of the chunk loop, it keeps per-lane LDS addresses from being hoisted out of
-// the loop: they are cheap to recompute, while keeping them all live would
-// spill registers to scratch memory.
-__device__ __forceinline__ int opaque_lane()
-{
-    int l = __lane_id();
-    asm volatile("" : "+v"(l));
-    return l;
 }
 
 template <int N> __device__ __forceinline__ void load_f32(float *dst, const float *src)
@@ -287,14 +286,14 @@ __device__ __forceinline__ float bounded_alpha(float z, float eA, float b)
 // function table), whose partial sums of squares are in sm.nrm.
 template <bool FULL, bool FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
-                                        const GateCtx &gc, int buf)
+                                        const GateCtx &gc)
 {
     typedef Cfg<T, DK, BV> Cf;
     typedef typename Vec<T>::two V2;
     typedef typename Vec<T>::eight_bytes V8;
     const int wv = wave_id();
     if (wv < Cf::EWAVES) {
-        const int lp = opaque_lane(), n16 = lp & 15, qr = lp >> 4;
+        const int lp = __lane_id(), n16 = lp & 15, qr = lp >> 4;
         const int I = wv / Cf::WPB, cp = (wv % Cf::WPB) * 16 + n16;
         const int r0 = 16 * I + 4 * qr;
         float bb[2] = {0.f, 0.f};
@@ -327,7 +326,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
             const float lead = ((qr > 0 ? qd[0] : 1.f) * (qr > 1 ? qd[1] : 1.f)) * (qr > 2 ? qd[2] : 1.f);
             const float tail = ((qr < 1 ? qd[1] : 1.f) * (qr < 2 ? qd[2] : 1.f)) * (qr < 3 ? qd[3] : 1.f);
             ebv[cc] = ((qd[0] * qd[1]) * qd[2]) * qd[3];
-            rb[cc] = __builtin_amdgcn_rcpf(ebv[cc]);                 // <= e^80
+            rb[cc] = __builtin_amdgcn_rcpf(ebv[cc]);                 // e^{-B} <= e^80
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 eL[cc][r] = lead * pl[r];
@@ -349,7 +348,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
                 ik = s2k > 0.f ? __builtin_amdgcn_rsqf(s2k) : 0.f;
                 iq = s2q > 0.f ? __builtin_amdgcn_rsqf(s2q) : 0.f;
             }
-            float kk[2], qq[2], kc[2], kd[2];
+            float kk[2], qq[2], kc[2];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 kk[cc] = in ? to_f32(R.k[r][cc]) : 0.f;
@@ -359,19 +358,20 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
                     qq[cc] *= iq;
                 }
                 kc[cc] = kk[cc] * sx[cc][r];              // e^{B - L_r} <= 1
-                kd[cc] = kc[cc] * rb[cc];                 // e^{-L_r} <= e^80
             }
             *reinterpret_cast<V2 *>(&sm.Kr[r0 + r][2 * cp]) =
                 pack2<T>(kk[0] * eL[0][r], kk[1] * eL[1][r]);
             if (OUT)
                 *reinterpret_cast<V2 *>(&sm.Qr[r0 + r][2 * cp]) =
                     pack2<T>(qq[0] * eL[0][r], qq[1] * eL[1][r]);
-            *reinterpret_cast<V2 *>(&sm.Kc[buf][r0 + r][2 * cp]) = pack2<T>(kc[0], kc[1]);
-            *reinterpret_cast<V2 *>(&sm.Kd[r0 + r][2 * cp]) = pack2<T>(kd[0], kd[1]);
+            *reinterpret_cast<V2 *>(&sm.Kc[r0 + r][2 * cp]) = pack2<T>(kc[0], kc[1]);
         }
-        if (qr == 0) *reinterpret_cast<f32x2 *>(&sm.eB[I][2 * cp]) = f32x2{ebv[0], ebv[1]};
+        if (qr == 0) {
+            *reinterpret_cast<f32x2 *>(&sm.eB[I][2 * cp]) = f32x2{ebv[0], ebv[1]};
+            *reinterpret_cast<f32x2 *>(&sm.eBr[I][2 * cp]) = f32x2{rb[0], rb[1]};
+        }
     }
-    const int to = 64 * wv + opaque_lane();     // threadIdx.x, recomputed
+    const int to = 64 * wv + __lane_id();
     if (to < Cf::C) sm.beta[to] = (FULL || to < nv) ? R.beta : 0.f;   // beta = 0 masks rows past the end
 #pragma unroll
     for (int m = 0; m < Cf::NVV; ++m) {
@@ -383,10 +383,10 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
 
 template <bool FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
-                                        const GateCtx &gc, int buf)
+                                        const GateCtx &gc)
 {
-    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED, OUT>(sm, R, nv, gc, buf);
-    else e_phase<false, FUSED, OUT>(sm, R, nv, gc, buf);
+    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED, OUT>(sm, R, nv, gc);
+    else e_phase<false, FUSED, OUT>(sm, R, nv, gc);
 }
 
 // Sum over the 16 lanes of a row of the wave (lanes 16 j .. 16 j + 15), with
@@ -409,7 +409,7 @@ __device__ __forceinline__ void norm_partials(Smem<T, DK, BV> &sm, const ChunkRe
     typedef Cfg<T, DK, BV> Cf;
     const int wv = wave_id();
     if (wv < Cf::EWAVES) {
-        const int lp = opaque_lane(), n16 = lp & 15, qr = lp >> 4;
+        const int lp = __lane_id(), n16 = lp & 15, qr = lp >> 4;
         const int I = wv / Cf::WPB, part = wv % Cf::WPB;
         const int r0 = 16 * I + 4 * qr;
 #pragma unroll
@@ -432,7 +432,7 @@ __device__ __forceinline__ void norm_partials(Smem<T, DK, BV> &sm, const ChunkRe
 // both products.  The products are taken transposed so that each lane ends
 // with four consecutive columns of one row.
 template <int I, int J, bool OUT, typename T, int DK, int BV>
-__device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp, int buf)
+__device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp)
 {
     typedef Path<T> PT;
     typedef typename Vec<T>::four V4;
@@ -441,7 +441,7 @@ __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp, i
 #pragma unroll
     for (int ks = 0; ks < DK / KS; ++ks) {
         const int kc = ks * KS + grp * KPL;
-        typename PT::frag col = load_frag<T>(&sm.Kc[buf][16 * J + n16][kc]);
+        typename PT::frag col = load_frag<T>(&sm.Kc[16 * J + n16][kc]);
         if (I > J + 1) {
             float x[KPL], f[KPL];
             PT::unpack(col, x);
@@ -469,30 +469,68 @@ __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp, i
         wa[i] = nb * accA[i];
         wp[i] = accP[i];
     }
-    *reinterpret_cast<V4 *>(&sm.An[r][16 * J + 4 * grp]) = pack4<T>(wa);
+    *reinterpret_cast<V4 *>(&sm.An[r - 16][16 * J + 4 * grp]) = pack4<T>(wa);
     if (OUT) *reinterpret_cast<V4 *>(&sm.P[r][16 * J + 4 * grp]) = pack4<T>(wp);
 }
 
-// Decay tables of the chunk for channel c: e^{E_J} = prod_{m<J} e^{B_m}
-// (J = 0..NB, the last being the whole-chunk decay) and prod_{m>J} e^{B_m}.
+// Decay tables of the chunk for channel c: prod_{m>J} e^{B_m} for each
+// sub-block J, and the whole-chunk decay prod_m e^{B_m}.
 template <typename T, int DK, int BV>
 __device__ __forceinline__ void decay_tables(Smem<T, DK, BV> &sm, int c)
 {
     constexpr int NB = Cfg<T, DK, BV>::NB;
-    float e[NB];
-#pragma unroll
-    for (int m = 0; m < NB; ++m) e[m] = sm.eB[m][c];
     float f = 1.f;
-#pragma unroll
-    for (int m = 0; m <= NB; ++m) {
-        sm.eE[m][c] = f;
-        if (m < NB) f *= e[m];
-    }
-    f = 1.f;
 #pragma unroll
     for (int m = NB - 1; m >= 0; --m) {
         sm.eTx[m][c] = f;
-        f *= e[m];
+        f *= sm.eB[m][c];
+    }
+    sm.eE[c] = f;
+}
+
+// Row operands of the state read-out for sub-blocks I >= 1 on the reference of
+// the chunk start: Kg = (K o e^{L}) e^{E_I} = K o e^{G} with e^{E_I} =
+// prod_{m<I} e^{B_m}, and Qg likewise.  Every factor here is at most 1, so a
+// product can only underflow, and one that does is a term below 1e-38 of its
+// row: nothing significant is lost.  A 16 x 16 block is one K = 16 product on
+// the matrix cores, Kg_blk^T = Diag(e^{E_I}) Kr_blk^T: the transposed block is
+// read in the layout of its rows, and the result lands as four consecutive
+// channels of a row per lane.  Waves 0 .. 7 share the (sub-block, channel
+// block) pairs.
+template <bool OUT, typename T, int DK, int BV>
+__device__ __forceinline__ void chunk_ref_rows(Smem<T, DK, BV> &sm, int wv)
+{
+    typedef Cfg<T, DK, BV> Cf;
+    typedef Path<T> PT;
+    typedef typename PT::quad Q4;
+    constexpr int NCB = DK / 16;                      // channel blocks
+    constexpr int NPAIR = (Cf::NB - 1) * NCB;
+    constexpr int NWK = 8;
+    if (wv >= NWK) return;
+    const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
+#pragma unroll
+    for (int p0 = 0; p0 < NPAIR; p0 += NWK) {
+        const int p = p0 + wv;
+        if (NPAIR % NWK == 0 || p < NPAIR) {
+            const int I = 1 + p / NCB, cb = p % NCB;
+            const int c = 16 * cb + n16;                  // channel of this lane's diagonal entry
+            float e = sm.eB[0][c];
+            for (int m = 1; m < I; ++m) e *= sm.eB[m][c];
+            float a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = 4 * grp + i == n16 ? e : 0.f;
+            const Q4 da = PT::to_quad(a);
+            const int col = 16 * cb + 4 * grp;
+            const Q4 kx = *reinterpret_cast<const Q4 *>(&sm.Kr[16 * I + n16][col]);
+            Q4 qx{};
+            if (OUT) qx = *reinterpret_cast<const Q4 *>(&sm.Qr[16 * I + n16][col]);
+            const f32x4 ky = PT::mma16q(da, kx, zero4());
+            *reinterpret_cast<Q4 *>(&sm.Kg[16 * (I - 1) + n16][col]) = PT::to_quad(ky);
+            if (OUT) {
+                const f32x4 qy = PT::mma16q(da, qx, zero4());
+                *reinterpret_cast<Q4 *>(&sm.Qg[16 * (I - 1) + n16][col]) = PT::to_quad(qy);
+            }
+        }
     }
 }
 
@@ -522,36 +560,28 @@ __device__ __forceinline__ float load_frag_tr(const float *x, int ld, int k0, in
 }
 
 // (K o e^G) S and (Q o e^G) S for row block I and the NV value tiles
-// vt0 .. vt0 + NV - 1.  The decay e^{E_I} from the chunk start to sub-block I
-// scales the state operand (one fragment serves both products); the decay
-// factors and the K, Q fragments of a k step serve every value tile.  Y comes
-// back in the D layout (rows of the block in 4 grp + i, value columns in n16);
-// Z transposed (value columns in 4 grp + i, rows in n16), as the output's
-// transposed product needs it.
-template <bool SCALE, int NV, bool OUT, typename T, int DK, int BV>
-__device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, int n16, int grp,
-                                         f32x4 (&Y)[NV], f32x4 *Zt)
+// vt0 .. vt0 + NV - 1, from the row operands kx, qx (16 rows, stride LDK: the
+// chunk-start-referenced Kg, Qg for I >= 1, K o e^L and Q o e^L for I = 0,
+// where L = G); the K, Q fragments of a k step serve every value tile, and one
+// state fragment serves both products.  Y comes back in the D layout (rows of
+// the block in 4 grp + i, value columns in n16); Z transposed (value columns in
+// 4 grp + i, rows in n16), as the output's transposed product needs it.
+template <int NV, bool OUT, typename T, int DK, int BV>
+__device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, const T *kx, const T *qx, int vt0,
+                                         int n16, int grp, f32x4 (&Y)[NV], f32x4 *Zt)
 {
+    typedef Cfg<T, DK, BV> Cf;
     typedef Path<T> PT;
     constexpr int KS = PT::KS, KPL = PT::KPL;
 #pragma unroll
     for (int ks = 0; ks < DK / KS; ++ks) {
         const int kc = ks * KS + grp * KPL;
-        float f[KPL];
-        if (SCALE) load_f32<KPL>(f, &sm.eE[I][kc]);
-        const typename PT::frag kr = load_frag<T>(&sm.Kr[16 * I + n16][kc]);
+        const typename PT::frag kr = load_frag<T>(kx + n16 * Cf::LDK + kc);
         typename PT::frag qr{};
-        if (OUT) qr = load_frag<T>(&sm.Qr[16 * I + n16][kc]);
+        if (OUT) qr = load_frag<T>(qx + n16 * Cf::LDK + kc);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            typename PT::frag s = load_frag<T>(&sm.ST[16 * (vt0 + v) + n16][kc]);
-            if (SCALE) {
-                float x[KPL];
-                PT::unpack(s, x);
-#pragma unroll
-                for (int e = 0; e < KPL; ++e) x[e] *= f[e];
-                s = PT::pack(x);
-            }
+            const typename PT::frag s = load_frag<T>(&sm.ST[16 * (vt0 + v) + n16][kc]);
             Y[v] = PT::mma(kr, s, Y[v]);
             if (OUT) Zt[v] = PT::mma(s, qr, Zt[v]);
         }
@@ -560,15 +590,17 @@ __device__ __forceinline__ void yz_block(Smem<T, DK, BV> &sm, int I, int vt0, in
 
 // State read-out of job (I, value tiles vt0 .. vt0 + NV - 1): Y and Z^T by
 // yz_block, then R = B (V - Y) stored transposed for the substitution.
-template <bool SCALE, int NV, bool OUT, typename T, int DK, int BV>
+template <int NV, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void readout_r(Smem<T, DK, BV> &sm, int I, int vt0, f32x4 *Zt)
 {
     typedef typename Vec<T>::four V4;
-    const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+    const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
     f32x4 Y[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) Y[v] = zero4();
-    yz_block<SCALE, NV, OUT>(sm, I, vt0, n16, grp, Y, Zt);
+    const T *kx = I > 0 ? &sm.Kg[16 * (I - 1)][0] : &sm.Kr[0][0];
+    const T *qx = I > 0 ? &sm.Qg[16 * (I - 1)][0] : &sm.Qr[0][0];
+    yz_block<NV, OUT>(sm, kx, qx, vt0, n16, grp, Y, Zt);
     const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * I + 4 * grp]);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -698,9 +730,11 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             norm_partials(sm, R);
             __syncthreads();
         }
-        e_phase<FUSED, OUT>(sm, R, rows_in(sv.bos, sv.eos, C), gc, 0);
+        e_phase<FUSED, OUT>(sm, R, rows_in(sv.bos, sv.eos, C), gc);
     }
     __syncthreads();
+    // the first chunk's Kg, Qg; read after B1
+    if (nchunks > 0) chunk_ref_rows<OUT>(sm, wv);
 
     // Per chunk: AP | YZ | U and the next chunk's E | SO.  The elementwise
     // phase of chunk c + 1 writes only tiles that chunk c no longer reads.
@@ -708,19 +742,30 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         const int64_t t0 = sv.bos + ch * C;
         const int nv = rows_in(t0, sv.eos, C);           // rows of this chunk in the sequence
         const bool more = ch + 1 < nchunks;
-        const int kbuf = (int)(ch & 1);                  // Kc buffer of this chunk
         if (more) load_chunk<FUSED, OUT>(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, z, beta, DV);
 
         // ================= AP
+        // (lane indices inside the loop come from __lane_id(), which the
+        // compiler recomputes in each phase rather than keeping every per-lane
+        // LDS address live across the loop)
         if (wv < NB) {
             // diagonal block I: A_II both ways round, P_II, then (I + A_II)^-1
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             const int I = wv;
             f32x4 accAt = zero4(), accA = zero4(), accPt = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / KS; ++ks) {
                 const int kc = ks * KS + grp * KPL;
-                const typename PT::frag fd = load_frag<T>(&sm.Kd[16 * I + n16][kc]);
+                // K o e^{-L} = (K o e^{B - L}) e^{-B}, each factor <= e^80
+                typename PT::frag fd = load_frag<T>(&sm.Kc[16 * I + n16][kc]);
+                {
+                    float x[KPL], f[KPL];
+                    PT::unpack(fd, x);
+                    load_f32<KPL>(f, &sm.eBr[I][kc]);
+#pragma unroll
+                    for (int e = 0; e < KPL; ++e) x[e] *= f[e];
+                    fd = PT::pack(x);
+                }
                 const typename PT::frag fk = load_frag<T>(&sm.Kr[16 * I + n16][kc]);
                 accAt = PT::mma(fd, fk, accAt);   // [r = n16][j = 4 grp + i]
                 accA = PT::mma(fk, fd, accA);     // [r = 4 grp + i][j = n16]
@@ -768,29 +813,46 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         } else if (wv < NB + 6) {
             // off-diagonal block pairs; the heavier (farther) ones first, so
             // that the four SIMDs get similar shares
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             switch (wv - NB) {
-                case 0: ap_pair<3, 0, OUT>(sm, n16, grp, kbuf); break;
-                case 1: ap_pair<2, 0, OUT>(sm, n16, grp, kbuf); break;
-                case 2: ap_pair<3, 1, OUT>(sm, n16, grp, kbuf); break;
-                case 3: ap_pair<1, 0, OUT>(sm, n16, grp, kbuf); break;
-                case 4: ap_pair<2, 1, OUT>(sm, n16, grp, kbuf); break;
-                default: ap_pair<3, 2, OUT>(sm, n16, grp, kbuf); break;
+                case 0: ap_pair<3, 0, OUT>(sm, n16, grp); break;
+                case 1: ap_pair<2, 0, OUT>(sm, n16, grp); break;
+                case 2: ap_pair<3, 1, OUT>(sm, n16, grp); break;
+                case 3: ap_pair<1, 0, OUT>(sm, n16, grp); break;
+                case 4: ap_pair<2, 1, OUT>(sm, n16, grp); break;
+                default: ap_pair<3, 2, OUT>(sm, n16, grp); break;
             }
         } else if (wv >= Cf::NW - 2) {
             // decay tables, one channel per thread
-            const int c = 64 * (wv - (Cf::NW - 2)) + opaque_lane();
+            const int c = 64 * (wv - (Cf::NW - 2)) + __lane_id();
             if (c < DK) decay_tables(sm, c);
         }
         __syncthreads();   // ---------------------------------------------- B1
         if (more) load_chunk<FUSED, OUT>(R, LOAD_VB, sv, t0 + C, q, k, v, g, z, beta, DV);
 
-        // ================= YZ: state read-out for row blocks 1.. and R = B (V - Y)
+        // ================= YZ: state read-out and R = B (V - Y); the state
+        // waves take their Kbar^T fragments before the next chunk's E
+        // overwrites K o e^{B - L}
         if (has_job) {
             W[0] = zero4();   // Z^T of the two blocks accumulates in W[0], W[1]
             W[1] = zero4();
-            if (jI > 0) readout_r<true, 2, OUT>(sm, jI, jvt, W);
-            else readout_r<false, 2, OUT>(sm, 0, jvt, W);
+            readout_r<2, OUT>(sm, jI, jvt, W);
+        }
+        if (state_wave) {
+            // (K o e^{G_n - G})^T fragments of this wave's state row tile:
+            // (K o e^{B - L}) read transposed, times prod_{m>J} e^{B_m}
+            const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
+            const int c = 16 * ct + n16;
+#pragma unroll
+            for (int ks = 0; ks < C / KS; ++ks) {
+                const int kj = ks * KS + grp * KPL;
+                const float f = sm.eTx[kj >> 4][c];
+                float x[KPL];
+                PT::unpack(load_frag_tr(&sm.Kc[0][0], Cf::LDK, ks * KS, 16 * ct, n16, grp), x);
+#pragma unroll
+                for (int e = 0; e < KPL; ++e) x[e] *= f;
+                sm.KbT[ct][ks][lp] = PT::pack(x);
+            }
         }
         // fused prologue: the next chunk's row norms, read by its E after B2
         if (FUSED && more) norm_partials(sm, R);
@@ -802,7 +864,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         constexpr int UW0 = Cf::EWAVES + NVT <= Cf::NW ? Cf::EWAVES : 0;
         if (wv >= UW0 && wv < UW0 + NVT) {
             typedef typename PT::quad Q4;
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             const int vt = wv - UW0;
             Q4 Ub[NB];
 #pragma unroll
@@ -812,7 +874,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 f32x4 X = f32x4{xr[0], xr[1], xr[2], xr[3]};
 #pragma unroll
                 for (int J = 0; J < I; ++J)
-                    X = PT::mma16q(*reinterpret_cast<const Q4 *>(&sm.An[16 * I + n16][16 * J + 4 * grp]),
+                    X = PT::mma16q(*reinterpret_cast<const Q4 *>(&sm.An[16 * I - 16 + n16][16 * J + 4 * grp]),
                                    Ub[J], X);
                 Ub[I] = PT::to_quad(
                     PT::mma16q(*reinterpret_cast<const Q4 *>(&sm.Tm[I][n16][4 * grp]), PT::to_quad(X),
@@ -824,29 +886,16 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         }
         // ================= the next chunk's elementwise phase (the substituting
         // waves do their share after their substitution)
-        if (more) e_phase<FUSED, OUT>(sm, R, rows_in(t0 + C, sv.eos, C), gc, kbuf ^ 1);
+        if (more) e_phase<FUSED, OUT>(sm, R, rows_in(t0 + C, sv.eos, C), gc);
         __syncthreads();   // ---------------------------------------------- B3
 
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
         if (state_wave) {
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
-            // (K o e^{G_n - G})^T fragments of this wave's state row tile:
-            // (K o e^{B - L}) read transposed, times prod_{m>J} e^{B_m}
+            const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             typename PT::frag kb[C / KS];
-            {
-                const int c = 16 * ct + n16;
 #pragma unroll
-                for (int ks = 0; ks < C / KS; ++ks) {
-                    const int kj = ks * KS + grp * KPL;
-                    const float f = sm.eTx[kj >> 4][c];
-                    float x[KPL];
-                    PT::unpack(load_frag_tr(&sm.Kc[kbuf][0][0], Cf::LDK, ks * KS, 16 * ct, n16, grp), x);
-#pragma unroll
-                    for (int e = 0; e < KPL; ++e) x[e] *= f;
-                    kb[ks] = PT::pack(x);
-                }
-            }
-            const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[NB][16 * ct + 4 * grp]);
+            for (int ks = 0; ks < C / KS; ++ks) kb[ks] = sm.KbT[ct][ks][lp];
+            const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[16 * ct + 4 * grp]);
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
                 f32x4 acc = W[vt] * gam;
@@ -861,7 +910,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             }
         }
         if (OUT && has_job) {
-            const int lp = opaque_lane(), n16 = lp & 15, grp = lp >> 4;
+            const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             // transposed blocks: lane holds O[16 jI + n16][16 (jvt + v) + 4 grp + i]
             const int nks = (16 * (jI + 1) + KS - 1) / KS;
             f32x4 acc[2] = {W[0], W[1]};
@@ -884,6 +933,8 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 }
             }
         }
+        // the next chunk's Kg, Qg (its E ran before B3)
+        if (more) chunk_ref_rows<OUT>(sm, wv);
         __syncthreads();   // ---------------------------------------------- B4
     }
 
