@@ -507,10 +507,14 @@ __device__ __forceinline__ void chunk_ref_rows(Smem<T, DK, BV> &sm, int wv)
     constexpr int NPAIR = (Cf::NB - 1) * NCB;
     constexpr int NWK = 8;
     if (wv >= NWK) return;
+    constexpr int NIT = (NPAIR + NWK - 1) / NWK;
     const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
+    // every load first (the compiler cannot tell that the stores do not alias
+    // them), then the products and stores
+    Q4 da[NIT], kx[NIT], qx[NIT];
 #pragma unroll
-    for (int p0 = 0; p0 < NPAIR; p0 += NWK) {
-        const int p = p0 + wv;
+    for (int it = 0; it < NIT; ++it) {
+        const int p = it * NWK + wv;
         if (NPAIR % NWK == 0 || p < NPAIR) {
             const int I = 1 + p / NCB, cb = p % NCB;
             const int c = 16 * cb + n16;                  // channel of this lane's diagonal entry
@@ -519,15 +523,22 @@ __device__ __forceinline__ void chunk_ref_rows(Smem<T, DK, BV> &sm, int wv)
             float a[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = 4 * grp + i == n16 ? e : 0.f;
-            const Q4 da = PT::to_quad(a);
+            da[it] = PT::to_quad(a);
             const int col = 16 * cb + 4 * grp;
-            const Q4 kx = *reinterpret_cast<const Q4 *>(&sm.Kr[16 * I + n16][col]);
-            Q4 qx{};
-            if (OUT) qx = *reinterpret_cast<const Q4 *>(&sm.Qr[16 * I + n16][col]);
-            const f32x4 ky = PT::mma16q(da, kx, zero4());
+            kx[it] = *reinterpret_cast<const Q4 *>(&sm.Kr[16 * I + n16][col]);
+            if (OUT) qx[it] = *reinterpret_cast<const Q4 *>(&sm.Qr[16 * I + n16][col]);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int p = it * NWK + wv;
+        if (NPAIR % NWK == 0 || p < NPAIR) {
+            const int I = 1 + p / NCB, cb = p % NCB;
+            const int col = 16 * cb + 4 * grp;
+            const f32x4 ky = PT::mma16q(da[it], kx[it], zero4());
             *reinterpret_cast<Q4 *>(&sm.Kg[16 * (I - 1) + n16][col]) = PT::to_quad(ky);
             if (OUT) {
-                const f32x4 qy = PT::mma16q(da, qx, zero4());
+                const f32x4 qy = PT::mma16q(da[it], qx[it], zero4());
                 *reinterpret_cast<Q4 *>(&sm.Qg[16 * (I - 1) + n16][col]) = PT::to_quad(qy);
             }
         }
