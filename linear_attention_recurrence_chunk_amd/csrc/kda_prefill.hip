@@ -570,6 +570,22 @@ __device__ __forceinline__ float load_frag_tr(const float *x, int ld, int k0, in
     return x[(k0 + grp) * ld + c0 + n16];
 }
 
+// Rows r0 .. r0 + 3 of column c0 + n16 of a row-major tile (row stride ld).
+// For 16-bit data it is one LDS transpose read, lane s = 4 i + j of each group
+// of 16 supplying the columns c0 + 4 j .. c0 + 4 j + 3 of row r0 + i.
+__device__ __forceinline__ void load_col4(const bf16 *x, int ld, int r0, int c0, int n16, float *out)
+{
+    const bf16x4 v = ds_read_tr4(x + (r0 + (n16 >> 2)) * ld + c0 + 4 * (n16 & 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = (float)v[i];
+}
+
+__device__ __forceinline__ void load_col4(const float *x, int ld, int r0, int c0, int n16, float *out)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = x[(r0 + i) * ld + c0 + n16];
+}
+
 // (K o e^G) S and (Q o e^G) S for row block I and the NV value tiles
 // vt0 .. vt0 + NV - 1, from the row operands kx, qx (16 rows, stride LDK: the
 // chunk-start-referenced Kg, Qg for I >= 1, K o e^L and Q o e^L for I = 0,
@@ -617,9 +633,9 @@ __device__ __forceinline__ void readout_r(Smem<T, DK, BV> &sm, int I, int vt0, f
     for (int v = 0; v < NV; ++v) {
         const int vt = vt0 + v;
         float rv[4];
+        load_col4(&sm.V[0][0], Cfg<T, DK, BV>::LDV, 16 * I + 4 * grp, 16 * vt, n16, rv);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            rv[i] = b4[i] * (to_f32(sm.V[16 * I + 4 * grp + i][16 * vt + n16]) - Y[v][i]);
+        for (int i = 0; i < 4; ++i) rv[i] = b4[i] * (rv[i] - Y[v][i]);
         *reinterpret_cast<V4 *>(&sm.RT[16 * vt + n16][16 * I + 4 * grp]) = pack4<T>(rv);
     }
 }
