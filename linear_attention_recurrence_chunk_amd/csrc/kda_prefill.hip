@@ -74,6 +74,12 @@ struct Cfg {
     static constexpr int LDK = DK + PAD;              // [token][channel] tiles
     static constexpr int LDC = C + PAD;               // [.][token] tiles
     static constexpr int LDV = BV + PAD;              // value slice rows
+    // Tiles read mostly as 16-byte MFMA fragments (lane (n16, grp): row n16,
+    // chunk grp) get rows padded by 32 bytes: with 64 four-byte banks that
+    // read is then free of bank conflicts (a 16-byte pad makes it two-way),
+    // at the price of two-way conflicts on their 8-byte accesses.
+    static constexpr int LDK2 = DK + 2 * PAD;
+    static constexpr int LDC2 = C + 2 * PAD;
     static constexpr int LD16 = 16 + PAD;             // 16 x 16 tiles
     static constexpr int WPB = DK / 32;               // E waves per sub-block
     static constexpr int EWAVES = NB * WPB;
@@ -105,8 +111,8 @@ struct Smem {
     T P[Cf::C][Cf::LDC];        // Tril((Q o e^G)(K o e^-G)^T)
     T An[Cf::C - 16][Cf::LDC];  // -A, blocks J < I (row r at r - 16: block 0 has none)
     T Tm[Cf::NB][16][Cf::LD16]; // (I + A_II)^-1
-    T ST[BV][Cf::LDK];          // state slice, transposed operand copy
-    T RT[BV][Cf::LDC];          // R^T, overwritten in place by U^T
+    T ST[BV][Cf::LDK2];         // state slice, transposed operand copy
+    T RT[BV][Cf::LDC2];         // R^T, overwritten in place by U^T
     T V[Cf::C][Cf::LDV];        // value slice
     float eB[Cf::NB][DK];       // e^{B_J}
     float eBr[Cf::NB][DK];      // e^{-B_J}
