@@ -284,9 +284,9 @@ __device__ __forceinline__ float bounded_alpha(float z, float eA, float b)
 
 // Elementwise phase for one chunk: from the raw g, k, q of this thread's item
 // (sub-block I, channels 2 cp and 2 cp + 1, rows 4 qr .. 4 qr + 3 of the
-// sub-block), the sub-block-local decays and the operand tiles K o e^L,
-// Q o e^L, K o e^{B-L}, K o e^-L and e^{B_I}; then
-// this thread's share of beta and of the value slice.  FULL: every row of the
+// sub-block), the sub-block-local decays, the operand tiles K o e^L, Q o e^L,
+// K o e^{B-L}, and e^{B_I}, e^{-B_I}; then this thread's share of beta and of
+// the value slice.  FULL: every row of the
 // chunk lies in the sequence.  FUSED: g comes from decay logits through the
 // bounded gate, and k and q are divided by their row norms (L2Norm of the
 // function table), whose partial sums of squares are in sm.nrm.
