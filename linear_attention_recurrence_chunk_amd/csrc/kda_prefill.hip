@@ -137,7 +137,7 @@ template <> struct Vec<float> { typedef f32x2 two; typedef f32x4 four; typedef f
 template <typename T, int DK, int BV>
 struct ChunkRegs {
     typedef Cfg<T, DK, BV> Cf;
-    f32x2 g[4];
+    f32x2 g[4];                         // fused prologue: the gate alpha, once computed
     typename Vec<T>::two z[4];          // fused prologue: decay logits instead of g
     typename Vec<T>::two k[4], q[4];
     typename Vec<T>::eight_bytes v[Cf::NVV];
@@ -292,7 +292,7 @@ __device__ __forceinline__ float bounded_alpha(float z, float eA, float b)
 // function table), whose partial sums of squares are in sm.nrm.
 template <bool FULL, bool FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
-                                        const GateCtx &gc)
+                                        const GateCtx &gc, bool pre)
 {
     typedef Cfg<T, DK, BV> Cf;
     typedef typename Vec<T>::two V2;
@@ -315,7 +315,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
             float a[4], pl[4], sl[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float ar = FUSED ? bounded_alpha(to_f32(R.z[r][cc]), gc.eA, bb[cc])
+                const float ar = FUSED ? (pre ? R.g[r][cc] : bounded_alpha(to_f32(R.z[r][cc]), gc.eA, bb[cc]))
                                        : __expf(R.g[r][cc]);
                 a[r] = (FULL || r0 + r < nv) ? ar : 1.f;
             }
@@ -389,10 +389,28 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
 
 template <bool FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
-                                        const GateCtx &gc)
+                                        const GateCtx &gc, bool pre = false)
 {
-    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED, OUT>(sm, R, nv, gc);
-    else e_phase<false, FUSED, OUT>(sm, R, nv, gc);
+    if (nv >= Cfg<T, DK, BV>::C) e_phase<true, FUSED, OUT>(sm, R, nv, gc, pre);
+    else e_phase<false, FUSED, OUT>(sm, R, nv, gc, pre);
+}
+
+// Fused prologue: the gate alpha of this thread's elementwise item, computed
+// ahead (on waves that are idle when it runs) into the registers g is not
+// using.  Rows past the end of the sequence are masked later, by the
+// elementwise phase.
+template <typename T, int DK, int BV>
+__device__ __forceinline__ void gate_items(const Smem<T, DK, BV> &sm, ChunkRegs<T, DK, BV> &R,
+                                           const GateCtx &gc)
+{
+    typedef Cfg<T, DK, BV> Cf;
+    const int wv = wave_id();
+    const int cp = (wv % Cf::WPB) * 16 + (__lane_id() & 15);
+    const f32x2 b2 = *reinterpret_cast<const f32x2 *>(&sm.bA[2 * cp]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) R.g[r][cc] = bounded_alpha(to_f32(R.z[r][cc]), gc.eA, b2[cc]);
 }
 
 // Sum over the 16 lanes of a row of the wave (lanes 16 j .. 16 j + 15), with
@@ -889,6 +907,9 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         }
         // fused prologue: the next chunk's row norms, read by its E after B2
         if (FUSED && more) norm_partials(sm, R);
+        // fused prologue: the state waves take their items' gate ahead
+        const bool pre = FUSED && state_wave && wv < Cf::EWAVES;
+        if (pre && more) gate_items(sm, R, gc);
         __syncthreads();   // ---------------------------------------------- B2
 
         // ================= U: forward substitution, one wave per value tile;
@@ -919,7 +940,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         }
         // ================= the next chunk's elementwise phase (the substituting
         // waves do their share after their substitution)
-        if (more) e_phase<FUSED, OUT>(sm, R, rows_in(t0 + C, sv.eos, C), gc);
+        if (more) e_phase<FUSED, OUT>(sm, R, rows_in(t0 + C, sv.eos, C), gc, pre);
         __syncthreads();   // ---------------------------------------------- B3
 
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
