@@ -116,6 +116,23 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                      "frac": _gbs(fb, ms) / HBM_PEAK_GBS,
                      "traffic": _traffic("kda_prefill.hip", "k3_prefill_8k_fused_prologue"),
                      "kernel": "kda::prefill_kernel<..., fused prologue>", "bytes_per_launch": fb}}
+    # the prefill with its attention output in fp32 (kda_chunk_fwd_ex)
+    o32 = torch.empty(x["v"].shape, dtype=torch.float32, device=dev)
+    sf32 = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+    def f32step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                      x["cu_seqlens"], chunk_size=w.chunk, out=o32, final_state=sf32,
+                      o_dtype=torch.float32)
+
+    ms, _ = time_launches(f32step, args.steps, args.warmup, torch)
+    pb = prefill_bytes(n_tok, n_seq, w.H, w.dk, w.dv, e, 4, x["initial_state"] is not None, True)
+    res["prefill_fp32_output"] = {
+        "workload": w.name, "ms_per_step": ms, "tokens/s": n_tok / (ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": _gbs(pb, ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": _gbs(pb, ms) / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda::prefill_kernel<..., fp32 o>", "bytes_per_launch": pb}}
+    del o32, sf32
     # output epilogue on the prefill's output rows
     rows = n_tok * w.H
     og = torch.empty_like(o)

@@ -116,6 +116,24 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd with the element type of o given apart: o_dtype is dtype or
+ * KDA_F32.  With bf16 inputs and o_dtype = KDA_F32, o = S_t^T q_t is written
+ * in fp32 without the final rounding to bf16: the attention output is kept in
+ * FP32 during training (page "Vecteurs, embeddings, espaces de
+ * representation", section "La precision numerique : FP32, BF16, FP8, FP4":
+ * the format table and the box "Limite importante").  The products inside
+ * still take bf16 operands with fp32 accumulation.  Any other o_dtype:
+ * KDA_ERR_UNSUPPORTED.  kda_chunk_fwd(...) is kda_chunk_fwd_ex(..., dtype,
+ * dtype, ...); every other argument is as there.
+ */
+kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int32_t H, int32_t d_k, int32_t d_v, int32_t chunk_size,
+                            kda_dtype dtype, kda_dtype o_dtype, void *o, float *final_state,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step: each of N requests appends one token and advances its own
  * state in place ("Glossaire", entry "Decode": bandwidth bound).
  *
@@ -174,6 +192,19 @@ kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void 
 kda_status kda_output_gate(const void *o_raw, const void *gate, const float *weight, float eps,
                            void *out, int64_t rows, int32_t d_v, kda_dtype dtype,
                            hipStream_t stream);
+
+/*
+ * kda_output_gate with the element types of o_raw and out given apart, each
+ * dtype or KDA_F32 (the gate logits are dtype): the epilogue of an fp32
+ * attention output (kda_chunk_fwd_ex with o_dtype = KDA_F32), with a bf16 or
+ * fp32 result.  out may alias o_raw only when o_dtype == out_dtype
+ * (KDA_ERR_UNSUPPORTED for out == o_raw otherwise).  kda_output_gate(...) is
+ * kda_output_gate_ex(o_raw, dtype, gate, weight, eps, out, dtype, rows, d_v,
+ * dtype, stream).
+ */
+kda_status kda_output_gate_ex(const void *o_raw, kda_dtype o_dtype, const void *gate,
+                              const float *weight, float eps, void *out, kda_dtype out_dtype,
+                              int64_t rows, int32_t d_v, kda_dtype dtype, hipStream_t stream);
 
 /*
  * ShortConv: causal depthwise convolution with 4 taps over each packed

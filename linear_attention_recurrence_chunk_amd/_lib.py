@@ -45,6 +45,9 @@ def library() -> ctypes.CDLL:
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                   vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                     i32, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_ex.restype = i32
     lib.kda_step_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_step_decode.restype = i32
     lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
@@ -52,6 +55,8 @@ def library() -> ctypes.CDLL:
     lib.kda_chunk_fwd_fused.restype = i32
     lib.kda_output_gate.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i32, i32, vp]
     lib.kda_output_gate.restype = i32
+    lib.kda_output_gate_ex.argtypes = [vp, i32, vp, vp, ctypes.c_float, vp, i32, i64, i32, i32, vp]
+    lib.kda_output_gate_ex.restype = i32
     lib.kda_short_conv.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, i32, vp]
     lib.kda_short_conv.restype = i32
     lib.kda_state_compose.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp]
@@ -117,9 +122,10 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
               g: torch.Tensor, beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None, output: bool = True
+              final_state: Optional[torch.Tensor] = None, output: bool = True,
+              o_dtype: Optional[torch.dtype] = None
               ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
-    """Chunkwise KDA prefill (kda_chunk_fwd).
+    """Chunkwise KDA prefill (kda_chunk_fwd; kda_chunk_fwd_ex for o_dtype).
 
     q, k [N_tok, H, d_k] or [B, T, H, d_k]; v like q with d_v; g like q (fp32);
     beta [N_tok, H] or [B, T, H] (fp32); initial_state [N, H, d_k, d_v] fp32 or
@@ -128,7 +134,8 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
     None).  ``out`` / ``final_state`` may be passed preallocated.
 
     output=False computes only the final states (o is None and q may be None);
-    v=None stands for zero values (d_v = d_k).
+    v=None stands for zero values (d_v = d_k).  o_dtype=torch.float32 with bf16
+    inputs writes o in fp32 (None: the input dtype).
     """
     if not output and not output_final_state and final_state is None:
         raise ValueError("nothing to compute: output=False needs the final state")
@@ -169,17 +176,27 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
         _need(initial_state, "initial_state", dtype=torch.float32, device=dev)
         if tuple(initial_state.shape) != sshape:
             raise ValueError(f"initial_state must have shape {sshape}")
-    out = _out(out, k.shape[:-1] + (dv,), k.dtype, dev) if output else None
+    odt = k.dtype if o_dtype is None else o_dtype
+    if odt not in (k.dtype, torch.float32):
+        raise ValueError(f"o_dtype must be {k.dtype} or torch.float32, got {o_dtype}")
+    out = _out(out, k.shape[:-1] + (dv,), odt, dev) if output else None
     if final_state is not None or output_final_state:
         final_state = _out(final_state, sshape, torch.float32, dev, "final_state")
     ws_bytes = workspace_size(num_seqs, n_tok, H, dk, chunk_size, k.dtype)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     lib = library()
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                           _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv, chunk_size,
-                           _DTYPES[k.dtype], _ptr(out), _ptr(final_state), _ptr(ws), ws_bytes,
-                           _stream(dev))
-    _check("kda_chunk_fwd", st)
+    if odt == k.dtype:
+        st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                               _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv, chunk_size,
+                               _DTYPES[k.dtype], _ptr(out), _ptr(final_state), _ptr(ws), ws_bytes,
+                               _stream(dev))
+        _check("kda_chunk_fwd", st)
+    else:
+        st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv,
+                                  chunk_size, _DTYPES[k.dtype], _DTYPES[odt], _ptr(out),
+                                  _ptr(final_state), _ptr(ws), ws_bytes, _stream(dev))
+        _check("kda_chunk_fwd_ex", st)
     return out, final_state
 
 
@@ -268,22 +285,42 @@ def chunk_fwd_fused(q_raw: torch.Tensor, k_raw: torch.Tensor, v: torch.Tensor, z
 
 
 def output_gate(o_raw: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor,
-                eps: float = 1e-5, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """RMSNorm(o_raw) * sigmoid(gate) over the last axis (kda_output_gate)."""
-    if o_raw.dtype not in _DTYPES:
-        raise ValueError(f"o_raw must be bf16 or fp32, got {o_raw.dtype}")
-    dev = o_raw.device
-    _gpu(dev)
+                eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """RMSNorm(o_raw) * sigmoid(gate) over the last axis (kda_output_gate;
+    kda_output_gate_ex when o_raw or the result is fp32 and the gate bf16).
+
+    The gate's dtype is the data type; o_raw may be that or fp32, and the
+    result out_dtype (None: o_raw's dtype) that or fp32.
+    """
+    _need(gate, "gate")
+    if gate.dtype not in _DTYPES:
+        raise ValueError(f"gate must be bf16 or fp32, got {gate.dtype}")
+    dt = gate.dtype
     _need(o_raw, "o_raw")
-    _need(gate, "gate", dtype=o_raw.dtype, device=dev)
+    if o_raw.dtype not in (dt, torch.float32):
+        raise ValueError(f"o_raw must be {dt} or torch.float32, got {o_raw.dtype}")
+    odt = o_raw.dtype if out_dtype is None else out_dtype
+    if odt not in (dt, torch.float32):
+        raise ValueError(f"out_dtype must be {dt} or torch.float32, got {out_dtype}")
+    dev = gate.device
+    _gpu(dev)
+    _need(o_raw, "o_raw", device=dev)
     _need(weight, "weight", dtype=torch.float32, ndim=(1,), device=dev)
     dv = o_raw.shape[-1]
     if gate.shape != o_raw.shape or tuple(weight.shape) != (dv,):
         raise ValueError("gate must match o_raw and weight must be [d_v]")
-    out = _out(out, o_raw.shape, o_raw.dtype, dev)
-    st = library().kda_output_gate(_ptr(o_raw), _ptr(gate), _ptr(weight), float(eps), _ptr(out),
-                                   o_raw.numel() // dv, dv, _DTYPES[o_raw.dtype], _stream(dev))
-    _check("kda_output_gate", st)
+    out = _out(out, o_raw.shape, odt, dev)
+    if o_raw.dtype == dt and odt == dt:
+        st = library().kda_output_gate(_ptr(o_raw), _ptr(gate), _ptr(weight), float(eps),
+                                       _ptr(out), o_raw.numel() // dv, dv, _DTYPES[dt],
+                                       _stream(dev))
+        _check("kda_output_gate", st)
+    else:
+        st = library().kda_output_gate_ex(_ptr(o_raw), _DTYPES[o_raw.dtype], _ptr(gate),
+                                          _ptr(weight), float(eps), _ptr(out), _DTYPES[odt],
+                                          o_raw.numel() // dv, dv, _DTYPES[dt], _stream(dev))
+        _check("kda_output_gate_ex", st)
     return out
 
 

@@ -9,7 +9,7 @@ namespace kda {
 hipError_t launch_prefill(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *s0, const int32_t *cu, int num_seqs,
                           int64_t seq_len, int H, int d, int chunk, bool is_bf16, void *o,
-                          float *sf, hipStream_t stream);
+                          bool o_f32, float *sf, hipStream_t stream);
 hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
                                 const void *z, const float *A_log, const float *b_alpha,
                                 const float *beta, const float *s0, const int32_t *cu,
@@ -19,7 +19,8 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
                          const float *beta, float *state, void *o, int64_t NH, int d,
                          bool is_bf16, hipStream_t stream);
 hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *w, float eps,
-                              void *out, int64_t rows, int dv, bool is_bf16, hipStream_t stream);
+                              void *out, int64_t rows, int dv, bool is_bf16, bool in_f32,
+                              bool out_f32, hipStream_t stream);
 hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, int nseq,
                              int64_t ntok, int C, float *state, void *y, bool is_bf16,
                              hipStream_t stream);
@@ -90,6 +91,26 @@ size_t kda_chunk_fwd_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t,
     return 0;  // the fused kernel keeps every intermediate on chip
 }
 
+kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int32_t H, int32_t d_k, int32_t d_v, int32_t chunk_size,
+                            kda_dtype dtype, kda_dtype o_dtype, void *o, float *final_state,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const kda_status st =
+        prefill_check(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, H,
+                      d_k, d_v, chunk_size, dtype, o, final_state, workspace, workspace_bytes, true);
+    if (st != KDA_OK) return st;
+    if (o_dtype != dtype && o_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return KDA_OK;
+    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
+    const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, cu_seqlens,
+                                             num_seqs, seq_len, H, d_k, 64, dtype == KDA_BF16, o,
+                                             o_dtype == KDA_F32, final_state, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *initial_state,
                          const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -97,16 +118,9 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          kda_dtype dtype, void *o, float *final_state, void *workspace,
                          size_t workspace_bytes, hipStream_t stream)
 {
-    const kda_status st =
-        prefill_check(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, H,
-                      d_k, d_v, chunk_size, dtype, o, final_state, workspace, workspace_bytes, true);
-    if (st != KDA_OK) return st;
-    if (num_seqs == 0) return KDA_OK;
-    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
-    const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, cu_seqlens,
-                                             num_seqs, seq_len, H, d_k, 64,
-                                             dtype == KDA_BF16, o, final_state, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return kda_chunk_fwd_ex(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens,
+                            H, d_k, d_v, chunk_size, dtype, dtype, o, final_state, workspace,
+                            workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void *v, const void *z,
@@ -134,11 +148,15 @@ kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void 
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_output_gate(const void *o_raw, const void *gate, const float *weight, float eps,
-                           void *out, int64_t rows, int32_t d_v, kda_dtype dtype,
-                           hipStream_t stream)
+kda_status kda_output_gate_ex(const void *o_raw, kda_dtype o_dtype, const void *gate,
+                              const float *weight, float eps, void *out, kda_dtype out_dtype,
+                              int64_t rows, int32_t d_v, kda_dtype dtype, hipStream_t stream)
 {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((o_dtype != dtype && o_dtype != KDA_F32) || (out_dtype != dtype && out_dtype != KDA_F32))
+        return KDA_ERR_UNSUPPORTED;
+    // in place only with equal element sizes
+    if (out == o_raw && o_raw && o_dtype != out_dtype) return KDA_ERR_UNSUPPORTED;
     if (rows < 0 || d_v < 1 || !(eps >= 0.f)) return KDA_ERR_SHAPE;
     if (d_v != 32 && d_v != 64 && d_v != 128) return KDA_ERR_UNSUPPORTED;
     if (rows == 0) return KDA_OK;
@@ -146,8 +164,16 @@ kda_status kda_output_gate(const void *o_raw, const void *gate, const float *wei
     if (misaligned(o_raw) || misaligned(gate) || misaligned(weight) || misaligned(out))
         return KDA_ERR_ALIGN;
     const hipError_t e =
-        kda::launch_output_gate(o_raw, gate, weight, eps, out, rows, d_v, dtype == KDA_BF16, stream);
+        kda::launch_output_gate(o_raw, gate, weight, eps, out, rows, d_v, dtype == KDA_BF16,
+                                o_dtype == KDA_F32, out_dtype == KDA_F32, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_output_gate(const void *o_raw, const void *gate, const float *weight, float eps,
+                           void *out, int64_t rows, int32_t d_v, kda_dtype dtype,
+                           hipStream_t stream)
+{
+    return kda_output_gate_ex(o_raw, dtype, gate, weight, eps, out, dtype, rows, d_v, dtype, stream);
 }
 
 kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,

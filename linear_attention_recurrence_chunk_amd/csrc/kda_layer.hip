@@ -18,27 +18,33 @@ namespace kda {
 
 // ---------------------------------------------------------------------------
 // Output epilogue.  One row = one (token, head): out = o~ / sqrt(mean(o~^2) +
-// eps) * w * sigma(gate).  A lane holds 16 bytes of a row (8 bf16 or 4 fp32);
-// the LPR lanes of a row reduce the sum of squares with xor shuffles.
-template <typename T, int DV>
-__global__ __launch_bounds__(256) void output_gate_kernel(const T *__restrict__ o_raw,
-                                                          const T *__restrict__ gate,
+// eps) * w * sigma(gate).  TI, TG, TO: the types of o~, the gate logits and
+// out (an fp32 o~ and out are the fp32-output option for bf16 data).  A lane
+// holds 16 bytes of the widest of them (8 bf16 or 4 fp32 elements); the LPR
+// lanes of a row reduce the sum of squares with xor shuffles.
+template <typename TI, typename TG, typename TO, int DV>
+__global__ __launch_bounds__(256) void output_gate_kernel(const TI *__restrict__ o_raw,
+                                                          const TG *__restrict__ gate,
                                                           const float *__restrict__ w, float eps,
-                                                          T *__restrict__ out, int64_t rows)
+                                                          TO *__restrict__ out, int64_t rows)
 {
-    constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
+    constexpr int WMAX = sizeof(TI) > sizeof(TG) ? (sizeof(TI) > sizeof(TO) ? sizeof(TI) : sizeof(TO))
+                                                 : (sizeof(TG) > sizeof(TO) ? sizeof(TG) : sizeof(TO));
+    constexpr int EPL = 16 / WMAX;               // elements per lane
     constexpr int LPR = DV / EPL;                // lanes per row
     constexpr int RPB = 256 / LPR;               // rows per block and step
     static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row mapping");
-    typedef T vec __attribute__((ext_vector_type(EPL)));
+    typedef TI vin __attribute__((ext_vector_type(EPL)));
+    typedef TG vgt __attribute__((ext_vector_type(EPL)));
+    typedef TO vec __attribute__((ext_vector_type(EPL)));
     const int t = threadIdx.x, lr = t % LPR, c0 = lr * EPL;
     float wv[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) wv[e] = w[c0 + e];
     for (int64_t row = (int64_t)blockIdx.x * RPB + t / LPR; row < rows;
          row += (int64_t)gridDim.x * RPB) {
-        const vec x = __builtin_nontemporal_load(reinterpret_cast<const vec *>(o_raw + row * DV + c0));
-        const vec gl = __builtin_nontemporal_load(reinterpret_cast<const vec *>(gate + row * DV + c0));
+        const vin x = __builtin_nontemporal_load(reinterpret_cast<const vin *>(o_raw + row * DV + c0));
+        const vgt gl = __builtin_nontemporal_load(reinterpret_cast<const vgt *>(gate + row * DV + c0));
         float xf[EPL], ss = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -52,45 +58,56 @@ __global__ __launch_bounds__(256) void output_gate_kernel(const T *__restrict__ 
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-to_f32(gl[e])));
-            y[e] = from_f32<T>(xf[e] * r * wv[e] * sg);
+            y[e] = from_f32<TO>(xf[e] * r * wv[e] * sg);
         }
         // a plain store: measured faster than a non-temporal one here
         *reinterpret_cast<vec *>(out + row * DV + c0) = y;
     }
 }
 
-template <typename T, int DV>
+template <typename TI, typename TG, typename TO, int DV>
 static hipError_t launch_output_gate_t(const void *o_raw, const void *gate, const float *w,
                                        float eps, void *out, int64_t rows, hipStream_t stream)
 {
-    constexpr int RPB = 256 / (DV / (16 / (int)sizeof(T)));
+    constexpr int WMAX = sizeof(TI) > sizeof(TG) ? (sizeof(TI) > sizeof(TO) ? sizeof(TI) : sizeof(TO))
+                                                 : (sizeof(TG) > sizeof(TO) ? sizeof(TG) : sizeof(TO));
+    constexpr int RPB = 256 / (DV / (16 / WMAX));
     const int64_t need = (rows + RPB - 1) / RPB;
     // four workgroups per CU stepping through the rows: with the plain stores,
     // 6.5 TB/s on 786432 rows of 128 bf16, against 6.3 with 8192 workgroups
     const int64_t blocks = need < 1024 ? need : 1024;
-    hipLaunchKernelGGL((output_gate_kernel<T, DV>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const T *)o_raw, (const T *)gate, w, eps, (T *)out, rows);
+    hipLaunchKernelGGL((output_gate_kernel<TI, TG, TO, DV>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, (const TI *)o_raw, (const TG *)gate, w, eps, (TO *)out, rows);
     return hipGetLastError();
 }
 
-hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *w, float eps,
-                              void *out, int64_t rows, int dv, bool is_bf16, hipStream_t stream)
+template <typename TI, typename TG, typename TO>
+static hipError_t launch_output_gate_d(const void *o_raw, const void *gate, const float *w,
+                                       float eps, void *out, int64_t rows, int dv,
+                                       hipStream_t stream)
 {
-    if (rows == 0) return hipSuccess;
-    if (is_bf16) {
-        switch (dv) {
-            case 32: return launch_output_gate_t<bf16, 32>(o_raw, gate, w, eps, out, rows, stream);
-            case 64: return launch_output_gate_t<bf16, 64>(o_raw, gate, w, eps, out, rows, stream);
-            case 128: return launch_output_gate_t<bf16, 128>(o_raw, gate, w, eps, out, rows, stream);
-        }
-    } else {
-        switch (dv) {
-            case 32: return launch_output_gate_t<float, 32>(o_raw, gate, w, eps, out, rows, stream);
-            case 64: return launch_output_gate_t<float, 64>(o_raw, gate, w, eps, out, rows, stream);
-            case 128: return launch_output_gate_t<float, 128>(o_raw, gate, w, eps, out, rows, stream);
-        }
+    switch (dv) {
+        case 32: return launch_output_gate_t<TI, TG, TO, 32>(o_raw, gate, w, eps, out, rows, stream);
+        case 64: return launch_output_gate_t<TI, TG, TO, 64>(o_raw, gate, w, eps, out, rows, stream);
+        case 128: return launch_output_gate_t<TI, TG, TO, 128>(o_raw, gate, w, eps, out, rows, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// is_bf16: the gate logits (and o~, out unless fp32 is asked for) are bf16.
+hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *w, float eps,
+                              void *out, int64_t rows, int dv, bool is_bf16, bool in_f32,
+                              bool out_f32, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+#define KDA_OG_ARGS o_raw, gate, w, eps, out, rows, dv, stream
+    if (!is_bf16) return launch_output_gate_d<float, float, float>(KDA_OG_ARGS);
+    if (in_f32)
+        return out_f32 ? launch_output_gate_d<float, bf16, float>(KDA_OG_ARGS)
+                       : launch_output_gate_d<float, bf16, bf16>(KDA_OG_ARGS);
+    return out_f32 ? launch_output_gate_d<bf16, bf16, float>(KDA_OG_ARGS)
+                   : launch_output_gate_d<bf16, bf16, bf16>(KDA_OG_ARGS);
+#undef KDA_OG_ARGS
 }
 
 // ---------------------------------------------------------------------------

@@ -62,6 +62,8 @@
 // loaded into registers one chunk ahead.
 #include "kda_common.hpp"
 
+#include <type_traits>
+
 namespace kda {
 
 template <typename T, int DK, int BV>
@@ -674,13 +676,14 @@ __device__ __forceinline__ int rows_in(int64_t t0, int64_t eos, int C)
 // FUSED: q and k arrive unnormalised and g is replaced by decay logits z with
 // the per-head gate parameters A_log [H] and b_alpha [H][DK].  OUT = false:
 // only the final state is computed (no o, q not read, and neither P nor
-// (Q o e^G) S is formed); v == nullptr stands for zero values.
-template <typename T, int DK, int BV, int DV, bool FUSED, bool OUT>
+// (Q o e^G) S is formed); v == nullptr stands for zero values.  TO: the type
+// of o (the input type, or fp32 for bf16 inputs).
+template <typename T, int DK, int BV, int DV, bool FUSED, bool OUT, typename TO>
 __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ s0, const int32_t *__restrict__ cu_seqlens, int num_seqs,
-    int64_t seq_len, int H, T *__restrict__ o, float *__restrict__ sfinal,
+    int64_t seq_len, int H, TO *__restrict__ o, float *__restrict__ sfinal,
     const T *__restrict__ z, const float *__restrict__ A_log, const float *__restrict__ b_alpha)
 {
     typedef Cfg<T, DK, BV> Cf;
@@ -977,13 +980,14 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             }
             const int row = 16 * jI + n16;
             if (row < nv) {
-                T *ob = o + (t0 * H + head) * DV + sv.v0;         // wave-uniform
+                typedef typename Vec<TO>::four VO;
+                TO *ob = o + (t0 * H + head) * DV + sv.v0;        // wave-uniform
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
                     float o4[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
-                    const uint32_t bo = __umul24((uint32_t)row, (uint32_t)(H * DV * sizeof(T))) +
-                                        (uint32_t)((16 * (jvt + v) + 4 * grp) * sizeof(T));
-                    *reinterpret_cast<V4 *>(reinterpret_cast<char *>(ob) + bo) = pack4<T>(o4);
+                    const uint32_t bo = __umul24((uint32_t)row, (uint32_t)(H * DV * sizeof(TO))) +
+                                        (uint32_t)((16 * (jvt + v) + 4 * grp) * sizeof(TO));
+                    *reinterpret_cast<VO *>(reinterpret_cast<char *>(ob) + bo) = pack4<TO>(o4);
                 }
             }
         }
@@ -1003,7 +1007,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     }
 }
 
-template <typename T, int D, int BV, bool FUSED, bool OUT>
+template <typename T, int D, int BV, bool FUSED, bool OUT, typename TO>
 static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *s0, const int32_t *cu,
                                    int num_seqs, int64_t seq_len, int H, void *o, float *sf,
@@ -1012,16 +1016,17 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 {
     const int64_t nwork = (int64_t)num_seqs * H * (D / BV);
     if (nwork == 0) return hipSuccess;
-    // token row strides in bytes (fp32 g is the widest) must fit 24 bits
+    // token row strides in bytes (fp32 g, or an fp32 o, is the widest) must fit 24 bits
     if ((int64_t)H * D * 4 >= (int64_t)1 << 24) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FUSED, OUT>), dim3((unsigned)nwork),
+    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FUSED, OUT, TO>), dim3((unsigned)nwork),
                        dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)q, (const T *)k,
-                       (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (T *)o, sf,
+                       (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (TO *)o, sf,
                        (const T *)z, A_log, b_alpha);
     return hipGetLastError();
 }
 
-template <bool FUSED, bool OUT>
+// O32: o in fp32 for bf16 inputs (only the unfused kernel with an output).
+template <bool FUSED, bool OUT, bool O32>
 static hipError_t launch_prefill_f(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *s0, const int32_t *cu,
                                    int num_seqs, int64_t seq_len, int H, int d, bool is_bf16,
@@ -1029,16 +1034,17 @@ static hipError_t launch_prefill_f(const void *q, const void *k, const void *v, 
                                    const float *b_alpha, hipStream_t stream)
 {
 #define KDA_PREFILL_ARGS q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, o, sf, z, A_log, b_alpha, stream
+    typedef typename std::conditional<O32, float, bf16>::type TOB;
     if (is_bf16) {
         switch (d) {
-            case 32: return launch_prefill_t<bf16, 32, 32, FUSED, OUT>(KDA_PREFILL_ARGS);
-            case 64: return launch_prefill_t<bf16, 64, 64, FUSED, OUT>(KDA_PREFILL_ARGS);
-            case 128: return launch_prefill_t<bf16, 128, 64, FUSED, OUT>(KDA_PREFILL_ARGS);
+            case 32: return launch_prefill_t<bf16, 32, 32, FUSED, OUT, TOB>(KDA_PREFILL_ARGS);
+            case 64: return launch_prefill_t<bf16, 64, 64, FUSED, OUT, TOB>(KDA_PREFILL_ARGS);
+            case 128: return launch_prefill_t<bf16, 128, 64, FUSED, OUT, TOB>(KDA_PREFILL_ARGS);
         }
-    } else {
+    } else if (!O32) {
         switch (d) {
-            case 32: return launch_prefill_t<float, 32, 32, FUSED, OUT>(KDA_PREFILL_ARGS);
-            case 64: return launch_prefill_t<float, 64, 32, FUSED, OUT>(KDA_PREFILL_ARGS);
+            case 32: return launch_prefill_t<float, 32, 32, FUSED, OUT, float>(KDA_PREFILL_ARGS);
+            case 64: return launch_prefill_t<float, 64, 32, FUSED, OUT, float>(KDA_PREFILL_ARGS);
         }
     }
 #undef KDA_PREFILL_ARGS
@@ -1048,14 +1054,19 @@ static hipError_t launch_prefill_f(const void *q, const void *k, const void *v, 
 hipError_t launch_prefill(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *s0, const int32_t *cu, int num_seqs,
                           int64_t seq_len, int H, int d, int chunk, bool is_bf16, void *o,
-                          float *sf, hipStream_t stream)
+                          bool o_f32, float *sf, hipStream_t stream)
 {
     if (chunk != 64) return hipErrorInvalidValue;
     if (!o)   // state only
-        return launch_prefill_f<false, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
-                                              is_bf16, o, sf, nullptr, nullptr, nullptr, stream);
-    return launch_prefill_f<false, true>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d, is_bf16,
-                                         o, sf, nullptr, nullptr, nullptr, stream);
+        return launch_prefill_f<false, false, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H,
+                                                     d, is_bf16, o, sf, nullptr, nullptr, nullptr,
+                                                     stream);
+    if (is_bf16 && o_f32)
+        return launch_prefill_f<false, true, true>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
+                                                   is_bf16, o, sf, nullptr, nullptr, nullptr,
+                                                   stream);
+    return launch_prefill_f<false, true, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
+                                                is_bf16, o, sf, nullptr, nullptr, nullptr, stream);
 }
 
 hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
@@ -1066,8 +1077,9 @@ hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void
 {
     if (chunk != 64) return hipErrorInvalidValue;
     if (!o) return hipErrorInvalidValue;
-    return launch_prefill_f<true, true>(q_raw, k_raw, v, nullptr, beta, s0, cu, num_seqs, seq_len, H,
-                                        d, is_bf16, o, sf, z, A_log, b_alpha, stream);
+    return launch_prefill_f<true, true, false>(q_raw, k_raw, v, nullptr, beta, s0, cu, num_seqs,
+                                               seq_len, H, d, is_bf16, o, sf, z, A_log, b_alpha,
+                                               stream);
 }
 
 }  // namespace kda

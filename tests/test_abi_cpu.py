@@ -30,7 +30,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == sorted(["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_step_decode",
                             "kda_status_string", "kda_version", "kda_chunk_fwd_fused",
-                            "kda_output_gate", "kda_short_conv", "kda_state_compose"])
+                            "kda_output_gate", "kda_short_conv", "kda_state_compose",
+                            "kda_chunk_fwd_ex", "kda_output_gate_ex"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -98,6 +99,27 @@ def test_chunk_fwd_rejects(kw, status):
 @gpu_visible
 def test_chunk_fwd_empty_batch_is_a_no_op():
     assert _fwd(num_seqs=0, total=0) == OK
+
+
+def _fwd_ex(o_dt, **kw):
+    a = dict(q=A, k=A, v=A, g=A, beta=A, s0=None, cu=None, num_seqs=1, total=128, H=2,
+             dk=64, dv=64, chunk=64, dt=1, o=A, sf=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _lib.library().kda_chunk_fwd_ex(
+        p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]), p(a["cu"]),
+        a["num_seqs"], a["total"], a["H"], a["dk"], a["dv"], a["chunk"], a["dt"], o_dt, p(a["o"]),
+        p(a["sf"]), p(a["ws"]), a["ws_bytes"], None)
+
+
+@gpu_visible
+def test_chunk_fwd_ex_rejects():
+    # o is the input type or fp32: bf16 o from fp32 inputs, or an unknown type, is refused
+    assert _fwd_ex(1, dt=0) == EUNSUP
+    assert _fwd_ex(7) == EUNSUP
+    assert _fwd_ex(0, q=None) == ENULL              # the common checks still apply
+    assert _fwd_ex(0, o=MIS) == EALIGN
+    assert _fwd_ex(0, num_seqs=0, total=0) == OK    # bf16 inputs, fp32 o, empty batch
 
 
 @gpu_visible
@@ -168,6 +190,13 @@ def test_layer_steps_reject():
     assert lib.kda_output_gate(p(A), None, p(A), 1e-5, p(A), 10, 128, 1, None) == ENULL
     assert lib.kda_output_gate(p(A), p(A), p(MIS), 1e-5, p(A), 10, 128, 1, None) == EALIGN
     assert lib.kda_output_gate(None, None, None, 1e-5, None, 0, 128, 1, None) == OK
+    # output gate with fp32 o~ or result: types, and no in-place call across element sizes
+    ex = lib.kda_output_gate_ex
+    assert ex(p(A), 7, p(A), p(A), 1e-5, p(A), 1, 10, 128, 1, None) == EUNSUP
+    assert ex(p(A), 0, p(A), p(A), 1e-5, p(A), 1, 10, 128, 0, None) == EUNSUP   # bf16 out of fp32 data
+    assert ex(p(A), 0, p(A), p(A), 1e-5, p(A), 1, 10, 128, 1, None) == EUNSUP   # out == o_raw, 4 vs 2 bytes
+    assert ex(p(A), 0, None, p(A), 1e-5, p(A + 4096), 0, 10, 128, 1, None) == ENULL
+    assert ex(None, 0, None, None, 1e-5, None, 0, 0, 128, 1, None) == OK
     # short conv: channels multiple of 4, sequence layout, pointers
     assert lib.kda_short_conv(p(A), p(A), None, 2, 10, 6, None, p(A), 1, None) == EUNSUP
     assert lib.kda_short_conv(p(A), p(A), None, 3, 10, 8, None, p(A), 1, None) == ESHAPE

@@ -200,3 +200,43 @@ def test_kcp_segments_compose_to_the_whole_sequence():
     e_in = _rel(_np(S_in[2]), s_pref[0])
     print(f"[parity] KCP: final={e_end:.3e}, M={e_m:.3e}, entering={e_in:.3e}")
     assert e_end <= 2e-2 and e_m <= 2e-2 and e_in <= 2e-2
+
+
+# fp32-output option: fp32 o~ (the fp32 attention output) and/or fp32 result,
+# bf16 gate logits (kda_output_gate_ex)
+@pytest.mark.parametrize("in32,out32", [(True, True), (True, False), (False, True)])
+@pytest.mark.parametrize("d", [128, 64, 32])
+def test_output_gate_fp32_variants(in32, out32, d):
+    gen = torch.Generator(device=dev).manual_seed(100 + d)
+    rows = 2 * 1000 + 3
+    o_raw = 3.0 * torch.randn(rows, d, generator=gen, device=dev)
+    if not in32:
+        o_raw = o_raw.to(torch.bfloat16)
+    gate = (2.0 * torch.randn(rows, d, generator=gen, device=dev)).to(torch.bfloat16)
+    w = torch.randn(d, generator=gen, device=dev)
+    odt = torch.float32 if out32 else torch.bfloat16
+    out = kda.output_gate(o_raw, gate, w, out_dtype=odt)
+    ref = L.output_gate(_np(o_raw), _np(gate), _np(w))
+    torch.cuda.synchronize()
+    assert out.dtype == odt
+    e = _rel(_np(out), ref)
+    print(f"[parity] output gate o~ {o_raw.dtype} -> {odt} d={d}: {e:.3e}")
+    # fp32 result: only fp32 rounding and the hardware exp / reciprocal steps
+    assert e <= (1e-5 if out32 else 1e-2)
+    if in32 == out32:
+        # equal element sizes: in place is allowed
+        again = kda.output_gate(o_raw, gate, w, out=o_raw, out_dtype=odt)
+        torch.cuda.synchronize()
+        assert again.data_ptr() == o_raw.data_ptr() and _rel(_np(o_raw), ref) <= 1e-5
+
+
+def test_output_gate_binding_checks_types():
+    o_raw = torch.randn(10, 64, device=dev)
+    gate = torch.randn(10, 64, device=dev).to(torch.bfloat16)
+    w = torch.ones(64, device=dev)
+    with pytest.raises(ValueError):
+        kda.output_gate(o_raw, gate, w, out_dtype=torch.float16)        # neither bf16 nor fp32
+    with pytest.raises(ValueError):
+        kda.output_gate(o_raw, gate, w, out=o_raw, out_dtype=torch.bfloat16)  # out must be bf16
+    with pytest.raises(ValueError):
+        kda.output_gate(o_raw.to(torch.float16), gate, w)               # o~ neither bf16 nor fp32

@@ -325,3 +325,26 @@ def test_binding_rejects_mismatched_outputs():
     M = torch.zeros(4, 32, 32, device=DEV)
     with pytest.raises(ValueError, match="out must have shape"):
         kda.state_compose(M, M, M, out=torch.empty(3, 32, 32, device=DEV))
+
+
+# ---------------------------------------------------------------------------
+# fp32 attention output from bf16 inputs (kda_chunk_fwd_ex)
+@pytest.mark.parametrize("d", [128, 64, 32])
+def test_prefill_fp32_output(d):
+    w = inputs.custom(H=3, dk=d, dv=d, seqlens=[130, 0, 64, 7], state_std=0.05,
+                      dtype=torch.bfloat16)
+    x = inputs.prefill_inputs(w, seed=90 + d, device=DEV)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
+    o16, s16 = kda.chunk_fwd(*args)
+    o32, s32 = kda.chunk_fwd(*args, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o32.dtype == torch.float32 and o16.dtype == torch.bfloat16
+    # the same arithmetic up to the store: the bf16 output is the rounded fp32 one,
+    # and the states do not depend on the output type
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    assert torch.equal(s32, s16)
+    cpu = lambda t: t.cpu()
+    o_ref, s_ref = oracle.forward(*(cpu(t) for t in args[:6]), x["cu_seqlens"].cpu().numpy())
+    eo, es = rel_err(o32, o_ref), rel_err(s32, s_ref)
+    report(f"prefill fp32 output d={d}", o=eo, state=es)
+    assert eo <= 2e-2 and es <= 2e-2
