@@ -287,7 +287,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="k3_prefill_8k")
     ap.add_argument("--decode-workload", default="k3_decode_256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
