@@ -87,7 +87,6 @@ struct Cfg {
     static constexpr int EWAVES = NB * WPB;
     static constexpr int NCT = DK / 16;               // state row tiles
     static constexpr int NVT = BV / 16;               // state column tiles
-    static constexpr int NTILE = NCT * NVT;
     static constexpr int SW0 = NW / 2;                // first state wave
     static constexpr int NREG = NVT > 2 ? NVT : 2;    // f32x4 tiles held per wave
     static constexpr int NJOB = NB * NVT;             // (row block, value tile) jobs
