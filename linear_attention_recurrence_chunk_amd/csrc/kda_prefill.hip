@@ -762,6 +762,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     // rescaled jobs and the other two one rescaled and one light job.
     constexpr int NP = NVT / 2;
     static_assert(NVT % 2 == 0 && NB * NP <= Cf::SW0, "job mapping");
+    static_assert(NB == 4 && Cf::NW == 16, "AP-phase wave roles: 4 diagonal, 6 pair, 2 table waves");
     const bool has_job = wv < NB * NP;
     const int jI = wv < (NB - 1) * NP ? 1 + wv / NP : 0;
     const int jvt = 2 * (wv % NP);                        // first of the two value tiles
@@ -863,21 +864,22 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             for (int i = 0; i < 4; ++i) mNd[i] = -Nd[i];
             X = PT::mma16q(PT::to_quad(mNd), PT::to_quad(X), X);  // (I - N^T)(...)
             *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(X);
-        } else if (wv < NB + 6) {
-            // off-diagonal block pairs; the heavier (farther) ones first, so
-            // that the four SIMDs get similar shares
+        } else if (wv < 8 || wv == 10 || wv == 11) {
+            // off-diagonal block pairs.  Wave w runs on SIMD w mod 4: the three
+            // pairs whose column needs a decay factor go to SIMDs 0, 1, 2, one
+            // each, and the three adjacent ones fill SIMDs 2 and 3
             const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
-            switch (wv - NB) {
-                case 0: ap_pair<3, 0, OUT>(sm, n16, grp); break;
-                case 1: ap_pair<2, 0, OUT>(sm, n16, grp); break;
-                case 2: ap_pair<3, 1, OUT>(sm, n16, grp); break;
-                case 3: ap_pair<1, 0, OUT>(sm, n16, grp); break;
-                case 4: ap_pair<2, 1, OUT>(sm, n16, grp); break;
-                default: ap_pair<3, 2, OUT>(sm, n16, grp); break;
+            switch (wv) {
+                case 4: ap_pair<3, 0, OUT>(sm, n16, grp); break;
+                case 5: ap_pair<2, 0, OUT>(sm, n16, grp); break;
+                case 6: ap_pair<3, 1, OUT>(sm, n16, grp); break;
+                case 7: ap_pair<1, 0, OUT>(sm, n16, grp); break;
+                case 10: ap_pair<3, 2, OUT>(sm, n16, grp); break;
+                default: ap_pair<2, 1, OUT>(sm, n16, grp); break;
             }
-        } else if (wv >= Cf::NW - 2) {
+        } else if (wv == 12 || wv == 13) {
             // decay tables, one channel per thread
-            const int c = 64 * (wv - (Cf::NW - 2)) + __lane_id();
+            const int c = 64 * (wv - 12) + __lane_id();
             if (c < DK) decay_tables(sm, c);
         }
         __syncthreads();   // ---------------------------------------------- B1
