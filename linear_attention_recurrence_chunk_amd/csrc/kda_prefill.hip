@@ -41,8 +41,8 @@
 //        e^{-B_I}; it runs in the previous chunk's U phase.
 //   AP   waves 0-3: diagonal block I of A and P (column operand K o e^{-L},
 //        formed from K o e^{B-L} and e^{-B_I}) and the inverse of I + A_II,
-//        kept in registers; waves 4-9: one pair of off-diagonal blocks of A
-//        and P; waves 14-15: the decay tables.
+//        kept in registers; waves 4-7, 10, 11: one pair of off-diagonal
+//        blocks of A and P; waves 12-13: the decay tables.
 //   YZ   one wave per (row block I, pair of value tiles): (K o e^G) S and
 //        (Q o e^G) S for its 16 rows and 32 value columns, from the tiles
 //        Kg, Qg built one chunk ahead, then R = B (V - (K o e^G) S); the state
