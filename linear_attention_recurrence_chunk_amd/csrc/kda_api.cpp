@@ -54,7 +54,6 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || total_tokens < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
     if (d_k != d_v || !head_size_ok(d_k, dt, true)) return KDA_ERR_UNSUPPORTED;
-    if (chunk != 64 && chunk != 128) return KDA_ERR_UNSUPPORTED;
     if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_SHAPE;
     if (!cu && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_SHAPE;
