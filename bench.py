@@ -301,7 +301,7 @@ def main():
                     help="also run a plain 1 GiB device copy (to scale HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU (the kernels shard across GPUs by (sequence, head) with no exchange, which is not implemented here); --gpus must be 1"}))
         sys.exit(2)
 
     import torch
