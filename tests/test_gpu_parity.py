@@ -278,6 +278,40 @@ def test_prefill_many_heads():
     assert eo <= 2e-2 and es <= 2e-2
 
 
+def _random_cases(n, seed=2024):
+    """Seeded random prefill shapes: head count, head size, type, a mix of
+    sequence lengths (empty, single tokens, sub-block and chunk edges, long
+    ragged ones), prefix states, chunk size and gate distribution."""
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129]
+    cases = []
+    for i in range(n):
+        dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+        d = int(rng.choice([32, 64] if dtype == torch.float32 else [32, 64, 128]))
+        nseq = int(rng.integers(1, 6))
+        lens = [int(rng.choice(edges)) if rng.random() < 0.5 else int(rng.integers(1, 400))
+                for _ in range(nseq)]
+        if sum(lens) == 0:
+            lens[0] = 1
+        cases.append(dict(H=int(rng.integers(1, 7)), dk=d, dv=d, seqlens=lens, dtype=dtype,
+                          state_std=float(rng.choice([0.0, 0.05])),
+                          chunk=int(rng.choice([64, 128])),
+                          extreme_heads=int(rng.integers(0, 2)), seed=100 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(16), ids=lambda c: f"seed{c['seed']}")
+def test_prefill_random_shapes(case):
+    case = dict(case)
+    seed = case.pop("seed")
+    w = inputs.custom(**case)
+    x = inputs.prefill_inputs(w, seed=seed, device=DEV)
+    eo, es = run_prefill(x, w.chunk)
+    report(f"prefill random {case}", o=eo, state=es)
+    tol = TOL[w.dtype]
+    assert eo <= tol and es <= tol
+
+
 # ---------------------------------------------------------------------------
 # state-only calls (o = NULL) and zero values (v = NULL)
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
