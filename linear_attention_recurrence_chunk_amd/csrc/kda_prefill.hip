@@ -117,7 +117,7 @@ struct Smem {
     T V[Cf::C][Cf::LDV];        // value slice
     float eB[Cf::NB][DK];       // e^{B_J}
     float eBr[Cf::NB][DK];      // e^{-B_J}
-    float eE[DK];               // whole-chunk decay prod_m e^{B_m}
+    float eE[2][DK];            // whole-chunk decay prod_m e^{B_m}, by chunk parity
     float eTx[Cf::NB][DK];      // prod_{m>J} e^{B_m}
     float beta[Cf::C];
     // (K o e^{G_n - G})^T fragments of the state waves, per (row tile, k step,
@@ -499,9 +499,10 @@ __device__ __forceinline__ void ap_pair(Smem<T, DK, BV> &sm, int n16, int grp)
 }
 
 // Decay tables of the chunk for channel c: prod_{m>J} e^{B_m} for each
-// sub-block J, and the whole-chunk decay prod_m e^{B_m}.
+// sub-block J, and the whole-chunk decay prod_m e^{B_m} (into buffer par of
+// two: the previous chunk's state update may still read the other).
 template <typename T, int DK, int BV>
-__device__ __forceinline__ void decay_tables(Smem<T, DK, BV> &sm, int c)
+__device__ __forceinline__ void decay_tables(Smem<T, DK, BV> &sm, int c, int par)
 {
     constexpr int NB = Cfg<T, DK, BV>::NB;
     float f = 1.f;
@@ -510,7 +511,7 @@ __device__ __forceinline__ void decay_tables(Smem<T, DK, BV> &sm, int c)
         sm.eTx[m][c] = f;
         f *= sm.eB[m][c];
     }
-    sm.eE[c] = f;
+    sm.eE[par][c] = f;
 }
 
 // Row operands of the state read-out for sub-blocks I >= 1 on the reference of
@@ -790,8 +791,10 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     // the first chunk's Kg, Qg; read after B1
     if (nchunks > 0) chunk_ref_rows<OUT>(sm, wv);
 
-    // Per chunk: AP | YZ | U and the next chunk's E | SO.  The elementwise
-    // phase of chunk c + 1 writes only tiles that chunk c no longer reads.
+    // Per chunk: AP | YZ | U and the next chunk's E | SO, with no barrier
+    // between SO and the next chunk's AP (three barriers a chunk).  The
+    // elementwise phase of chunk c + 1 writes only tiles that chunk c no longer
+    // reads.
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = sv.bos + ch * C;
         const int nv = rows_in(t0, sv.eos, C);           // rows of this chunk in the sequence
@@ -880,7 +883,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         } else if (wv == 12 || wv == 13) {
             // decay tables, one channel per thread
             const int c = 64 * (wv - 12) + __lane_id();
-            if (c < DK) decay_tables(sm, c);
+            if (c < DK) decay_tables(sm, c, (int)(ch & 1));
         }
         __syncthreads();   // ---------------------------------------------- B1
         if (more) load_chunk<FUSED, OUT>(R, LOAD_VB, sv, t0 + C, q, k, v, g, z, beta, DV);
@@ -945,6 +948,16 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         // ================= the next chunk's elementwise phase (the substituting
         // waves do their share after their substitution)
         if (more) e_phase<FUSED, OUT>(sm, R, rows_in(t0 + C, sv.eos, C), gc, pre);
+        // the P fragments of this wave's output blocks, read before B3: the
+        // next chunk's AP work rewrites P beside the output
+        const int nks = (16 * (jI + 1) + KS - 1) / KS;
+        typename PT::frag pfr[(C + KS - 1) / KS];
+        if (OUT && has_job) {
+            const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
+#pragma unroll
+            for (int ks = 0; ks < (C + KS - 1) / KS; ++ks)
+                if (ks < nks) pfr[ks] = load_frag<T>(&sm.P[16 * jI + n16][ks * KS + grp * KPL]);
+        }
         __syncthreads();   // ---------------------------------------------- B3
 
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
@@ -953,7 +966,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             typename PT::frag kb[C / KS];
 #pragma unroll
             for (int ks = 0; ks < C / KS; ++ks) kb[ks] = sm.KbT[ct][ks][lp];
-            const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[16 * ct + 4 * grp]);
+            const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[ch & 1][16 * ct + 4 * grp]);
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
                 f32x4 acc = W[vt] * gam;
@@ -970,14 +983,14 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         if (OUT && has_job) {
             const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             // transposed blocks: lane holds O[16 jI + n16][16 (jvt + v) + 4 grp + i]
-            const int nks = (16 * (jI + 1) + KS - 1) / KS;
             f32x4 acc[2] = {W[0], W[1]};
-            for (int ks = 0; ks < nks; ++ks) {
+#pragma unroll
+            for (int ks = 0; ks < (C + KS - 1) / KS; ++ks) {
+                if (ks >= nks) break;
                 const int kj = ks * KS + grp * KPL;
-                const typename PT::frag pf = load_frag<T>(&sm.P[16 * jI + n16][kj]);
 #pragma unroll
                 for (int v = 0; v < 2; ++v)
-                    acc[v] = PT::mma(load_frag<T>(&sm.RT[16 * (jvt + v) + n16][kj]), pf, acc[v]);
+                    acc[v] = PT::mma(load_frag<T>(&sm.RT[16 * (jvt + v) + n16][kj]), pfr[ks], acc[v]);
             }
             const int row = 16 * jI + n16;
             if (row < nv) {
@@ -992,9 +1005,11 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 }
             }
         }
-        // the next chunk's Kg, Qg (its E ran before B3)
+        // the next chunk's Kg, Qg (its E ran before B3).  No barrier follows:
+        // the next chunk's AP work runs beside this output and state update,
+        // which read P from registers and the whole-chunk decay from the other
+        // buffer, and it writes nothing else they read
         if (more) chunk_ref_rows<OUT>(sm, wv);
-        __syncthreads();   // ---------------------------------------------- B4
     }
 
     if (sfinal && state_wave) {
