@@ -53,10 +53,10 @@
 //   U    one wave per 16 value columns: the forward substitution (for d <= 64
 //        on waves that have no elementwise work).
 //   SO   the read-out waves: their two blocks of O = (Q o e^G) S + P U,
-//        stored to o, then a share of the next chunk's Kg, Qg (diagonal
-//        scalings on the matrix cores); waves 8 ..: one state row tile each,
+//        stored to o; waves 8 ..: one state row tile each,
 //        S' = Diag(gamma) S + Kbar^T U, the state staying in their registers
-//        across chunks.
+//        across chunks; then every wave a share of the next chunk's Kg, Qg
+//        (diagonal scalings on the matrix cores).
 // Contractions run on the matrix cores (v_mfma_f32_16x16x32_bf16 and
 // v_mfma_f32_16x16x16_bf16, or v_mfma_f32_16x16x4_f32 for fp32 inputs) with
 // fp32 accumulation; operands are rounded to the input type.  The fp32 state
@@ -523,8 +523,8 @@ __device__ __forceinline__ void decay_tables(Smem<T, DK, BV> &sm, int c, int par
 // row: nothing significant is lost.  A 16 x 16 block is one K = 16 product on
 // the matrix cores, Kg_blk^T = Diag(e^{E_I}) Kr_blk^T: the transposed block is
 // read in the layout of its rows, and the result lands as four consecutive
-// channels of a row per lane.  Waves 0 .. 7 share the (sub-block, channel
-// block) pairs.
+// channels of a row per lane.  All waves share the (sub-block, channel
+// block) pairs, waves 0 .. 7 taking the extra ones.
 template <bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void chunk_ref_rows(Smem<T, DK, BV> &sm, int wv)
 {
@@ -533,7 +533,7 @@ __device__ __forceinline__ void chunk_ref_rows(Smem<T, DK, BV> &sm, int wv)
     typedef typename PT::quad Q4;
     constexpr int NCB = DK / 16;                      // channel blocks
     constexpr int NPAIR = (Cf::NB - 1) * NCB;
-    constexpr int NWK = 8;
+    constexpr int NWK = Cf::NW;
     if (wv >= NWK) return;
     constexpr int NIT = (NPAIR + NWK - 1) / NWK;
     const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
