@@ -41,7 +41,7 @@
 //        e^{-B_I}; it runs in the previous chunk's U phase.
 //   AP   waves 0-3: diagonal block I of A and P (column operand K o e^{-L},
 //        formed from K o e^{B-L} and e^{-B_I}) and the inverse of I + A_II,
-//        kept in registers; waves 4-7, 10, 11: one pair of off-diagonal
+//        kept in registers; waves 4-8, 10: one pair of off-diagonal
 //        blocks of A and P; waves 12-13: the decay tables.  It runs beside the
 //        previous chunk's SO phase, with no barrier between them: three
 //        barriers a chunk.
@@ -869,21 +869,22 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             for (int i = 0; i < 4; ++i) mNd[i] = -Nd[i];
             X = PT::mma16q(PT::to_quad(mNd), PT::to_quad(X), X);  // (I - N^T)(...)
             *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(X);
-        } else if (wv < 8 || wv == 10 || wv == 11) {
+        } else if (wv < 9 || wv == 10) {
             // off-diagonal block pairs.  Wave w runs on SIMD w mod 4: the three
             // pairs whose column needs a decay factor go to SIMDs 1, 2, 3, one
-            // each, and the three adjacent ones to SIMDs 0, 2, 3.  This phase
-            // also runs the previous chunk's output blocks, the heaviest (row
-            // block 3) on waves 4 and 5 and the lightest (row block 0) on 6 and
-            // 7, so the farthest pair (3, 0) goes to wave 7
+            // each, and the three adjacent ones to SIMDs 0, 0, 2 (SIMDs 0 and 1
+            // also have the decay tables).  This phase also runs the previous
+            // chunk's output blocks, the heaviest (row block 3) on waves 4 and 5
+            // and the lightest (row block 0) on 6 and 7, so the farthest pair
+            // (3, 0) goes to wave 7
             const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             switch (wv) {
                 case 4: ap_pair<1, 0, OUT>(sm, n16, grp); break;
                 case 5: ap_pair<2, 0, OUT>(sm, n16, grp); break;
                 case 6: ap_pair<3, 1, OUT>(sm, n16, grp); break;
                 case 7: ap_pair<3, 0, OUT>(sm, n16, grp); break;
-                case 10: ap_pair<3, 2, OUT>(sm, n16, grp); break;
-                default: ap_pair<2, 1, OUT>(sm, n16, grp); break;
+                case 8: ap_pair<2, 1, OUT>(sm, n16, grp); break;
+                default: ap_pair<3, 2, OUT>(sm, n16, grp); break;
             }
         } else if (wv == 12 || wv == 13) {
             // decay tables, one channel per thread
