@@ -49,7 +49,8 @@
 //        (Q o e^G) S for its 16 rows and 32 value columns, from the tiles
 //        Kg, Qg built one chunk ahead, then R = B (V - (K o e^G) S); the state
 //        waves take their Kbar^T fragments (K o e^{B-L} through the LDS
-//        transpose read, times the decay to the chunk end) into LDS.
+//        transpose read, times the decay to the chunk end) into registers,
+//        where they stay until the state update.
 //   U    one wave per 16 value columns: the forward substitution (for d <= 64
 //        on waves that have no elementwise work).
 //   SO   the read-out waves: their two blocks of O = (Q o e^G) S + P U,
@@ -122,9 +123,6 @@ struct Smem {
     float eE[2][DK];            // whole-chunk decay prod_m e^{B_m}, by chunk parity
     float eTx[Cf::NB][DK];      // prod_{m>J} e^{B_m}
     float beta[Cf::C];
-    // (K o e^{G_n - G})^T fragments of the state waves, per (row tile, k step,
-    // lane): built in the read-out phase, used in the state update
-    typename Path<T>::frag KbT[Cf::NCT][Cf::C / Path<T>::KS][64];
     float nrm[2][Cf::C][Cf::WPB];  // fused prologue: partial sums of squares of k, q rows
     float bA[DK];                  // fused prologue: decay bias b_alpha^h of the head
 };
@@ -902,8 +900,11 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             W[1] = zero4();
             readout_r<2, OUT>(sm, jI, jvt, W);
         }
+        // (K o e^{G_n - G})^T fragments of a state wave's row tile, kept in its
+        // registers until its state update (the next chunk's E overwrites
+        // K o e^{B - L} before then)
+        typename PT::frag kbr[C / KS];
         if (state_wave) {
-            // (K o e^{G_n - G})^T fragments of this wave's state row tile:
             // (K o e^{B - L}) read transposed, times prod_{m>J} e^{B_m}
             const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
             const int c = 16 * ct + n16;
@@ -915,7 +916,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 PT::unpack(load_frag_tr(&sm.Kc[0][0], Cf::LDK, ks * KS, 16 * ct, n16, grp), x);
 #pragma unroll
                 for (int e = 0; e < KPL; ++e) x[e] *= f;
-                sm.KbT[ct][ks][lp] = PT::pack(x);
+                kbr[ks] = PT::pack(x);
             }
         }
         // fused prologue: the next chunk's row norms, read by its E after B2
@@ -969,9 +970,6 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         // ================= SO: S' = Diag(gamma) S + Kbar^T U; O = Z + P U
         if (state_wave) {
             const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
-            typename PT::frag kb[C / KS];
-#pragma unroll
-            for (int ks = 0; ks < C / KS; ++ks) kb[ks] = sm.KbT[ct][ks][lp];
             const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sm.eE[ch & 1][16 * ct + 4 * grp]);
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt) {
@@ -979,7 +977,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
 #pragma unroll
                 for (int ks = 0; ks < C / KS; ++ks) {
                     const int kj = ks * KS + grp * KPL;
-                    acc = PT::mma(kb[ks], load_frag<T>(&sm.RT[16 * vt + n16][kj]), acc);
+                    acc = PT::mma(kbr[ks], load_frag<T>(&sm.RT[16 * vt + n16][kj]), acc);
                 }
                 W[vt] = acc;
                 float s4[4] = {acc[0], acc[1], acc[2], acc[3]};
