@@ -844,29 +844,43 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 pv[i] = jl <= n16 ? accPt[i] : 0.f;
             }
             if (OUT) *reinterpret_cast<V4 *>(&sm.P[16 * I + n16][16 * I + 4 * grp]) = pack4<T>(pv);
-            // A lane's values of X in the A layout are those of X^T in the D
-            // layout.  So mma16(Xd, Xa), which multiplies X^T by X^T, returns
-            // (X^2)^T in the D layout, i.e. X^2 in the A layout: every power of
-            // N comes in both layouts without a transpose through LDS.
+            // (I + N)^-1 by recursive block inversion.  Let D_b be the
+            // block-diagonal matrix of the inverses of the b x b diagonal blocks
+            // of I + N, and F_b the part of N that lies in the lower-left b x b
+            // block of each 2b x 2b diagonal block.  Then D_2b = D_b - D_b F_b D_b;
+            // D_1 = I gives D_2 = I - F_1, and three more levels reach D_16.
+            // Every intermediate is a block of the true inverse, whose entries
+            // stay small when the keys of a sub-block are alike (the
+            // power-series product (I - N)(I + N^2)(I + N^4)(I + N^8) instead
+            // forms powers that grow like binomial coefficients and cancel).
+            // Layouts: a lane's values of X in the A layout (X[n16][4 grp + i])
+            // are those of X^T in the D layout (X[4 grp + i][n16]), so a product
+            // X Y comes in the D layout from mma16(X in A, Y in D) and in the A
+            // layout from mma16(Y in D, X in A).  D_b is kept in both layouts
+            // (fp32; rounded to the input type only as an operand).
             typedef typename PT::quad Q4;
-            const Q4 na = PT::to_quad(Na), nd = PT::to_quad(Nd);
-            const Q4 n2d = PT::to_quad(PT::mma16q(na, nd, zero4()));
-            const Q4 n2a = PT::to_quad(PT::mma16q(nd, na, zero4()));
-            const Q4 n4d = PT::to_quad(PT::mma16q(n2a, n2d, zero4()));
-            const Q4 n4a = PT::to_quad(PT::mma16q(n2d, n2a, zero4()));
-            // T^T = (I - N^T)(I + (N^2)^T)(I + (N^4)^T)(I + (N^8)^T) (the factors
-            // commute), built in the D layout, which holds T in the A layout:
-            // the lane ends with T[n16][4 grp + i]
-            f32x4 X = PT::mma16q(n4d, n4a, zero4());              // (N^8)^T
+            // F_b holds N[r][c] where r, c share a 2b block, r in its lower half
+            // and c in its upper half
+            auto in_f = [](int r, int c, int bs) { return (r ^ c) < 2 * bs && (r & bs) && !(c & bs); };
+            f32x4 Da, Dd;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) X[i] += (4 * grp + i == n16) ? 1.f : 0.f;
-            X = PT::mma16q(n4d, PT::to_quad(X), X);                // (I + (N^4)^T)(...)
-            X = PT::mma16q(n2d, PT::to_quad(X), X);                // (I + (N^2)^T)(...)
-            float mNd[4];
+            for (int i = 0; i < 4; ++i) {
+                const int jl = 4 * grp + i;
+                Da[i] = (jl == n16 ? 1.f : 0.f) - (in_f(n16, jl, 1) ? Na[i] : 0.f);
+                Dd[i] = (jl == n16 ? 1.f : 0.f) - (in_f(jl, n16, 1) ? Nd[i] : 0.f);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mNd[i] = -Nd[i];
-            X = PT::mma16q(PT::to_quad(mNd), PT::to_quad(X), X);  // (I - N^T)(...)
-            *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(X);
+            for (int bs = 2; bs < 16; bs *= 2) {
+                float Fa[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Fa[i] = in_f(n16, 4 * grp + i, bs) ? Na[i] : 0.f;
+                const Q4 da = PT::to_quad(Da);
+                const Q4 yd = PT::to_quad(PT::mma16q(PT::to_quad(Fa), PT::to_quad(Dd), zero4()));  // F D
+                Da -= PT::mma16q(yd, da, zero4());                                                   // D F D
+                if (bs < 8) Dd -= PT::mma16q(da, yd, zero4());
+            }
+            // the lane ends with T[n16][4 grp + i], T = (I + A_II)^-1
+            *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(Da);
         } else if (wv < 9 || wv == 10) {
             // off-diagonal block pairs.  Wave w runs on SIMD w mod 4: the three
             // pairs whose column needs a decay factor go to SIMDs 1, 2, 3, one

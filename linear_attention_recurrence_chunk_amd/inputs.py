@@ -53,6 +53,18 @@ class Workload:
     extreme_sigma: float = 0.5
     state_std: float = 0.0                       # 0 -> no initial state
     decode_requests: int = 0                     # >0 -> a one-token decode workload
+    # Correlated keys (stress of the in-chunk solve): with key_block > 0, the
+    # keys of each run of key_block tokens from a sequence start share one
+    # random unit direction b, k_t = normalise(b + key_eps * n_t), n_t ~
+    # N(0, 1/d_k) per channel (|n_t| ~ 1).  key_block = 0: i.i.d. keys.
+    key_block: int = 0
+    key_eps: float = 0.0
+    # beta = beta_const everywhere when given, else sigmoid(N(beta_mu, beta_sigma))
+    beta_mu: float = 0.0
+    beta_sigma: float = 1.0
+    beta_const: Optional[float] = None
+    # g = gate_const everywhere when given (0: no decay), else the gate above
+    gate_const: Optional[float] = None
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -113,6 +125,23 @@ def sequence_lengths(w: Workload, seed: int) -> List[int]:
     return [w.T] * w.B
 
 
+def _correlated_keys(lens, w: Workload, gen, device) -> torch.Tensor:
+    """Keys that share a direction within runs of w.key_block tokens of each
+    sequence (see Workload)."""
+    n_tok, H, dk = int(sum(lens)), w.H, w.dk
+    blk_of = []
+    nblk = 0
+    for L in lens:
+        blk_of.append(torch.arange(L) // w.key_block + nblk)
+        nblk += (L + w.key_block - 1) // w.key_block
+    idx = torch.cat(blk_of).to(device) if blk_of else torch.zeros(0, dtype=torch.int64, device=device)
+    base = _unit_rows((max(nblk, 1), H, dk), gen, device, torch.float32)
+    noise = torch.randn((n_tok, H, dk), generator=gen, device=device, dtype=torch.float32)
+    x = base[idx] + (w.key_eps / dk ** 0.5) * noise
+    x = x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+    return x.to(w.dtype)
+
+
 def prefill_inputs(w: Workload, seed: int, device="cpu") -> dict:
     """q, k [N_tok, H, dk]; v [N_tok, H, dv]; g [N_tok, H, dk] fp32; beta
     [N_tok, H] fp32; initial_state [N, H, dk, dv] fp32 or None; cu_seqlens
@@ -122,11 +151,18 @@ def prefill_inputs(w: Workload, seed: int, device="cpu") -> dict:
     gen = _gen(seed, device)
     H, dk, dv = w.H, w.dk, w.dv
     q = _unit_rows((n_tok, H, dk), gen, device, w.dtype)
-    k = _unit_rows((n_tok, H, dk), gen, device, w.dtype)
+    if w.key_block > 0:
+        k = _correlated_keys(lens, w, gen, device)
+    else:
+        k = _unit_rows((n_tok, H, dk), gen, device, w.dtype)
     v = torch.randn((n_tok, H, dv), generator=gen, device=device, dtype=torch.float32).to(w.dtype)
     g = _gate((n_tok, H, dk), H, w, gen, device)
+    if w.gate_const is not None:
+        g.fill_(w.gate_const)
     beta = torch.sigmoid(torch.randn((n_tok, H), generator=gen, device=device,
-                                     dtype=torch.float32))
+                                     dtype=torch.float32) * w.beta_sigma + w.beta_mu)
+    if w.beta_const is not None:
+        beta.fill_(w.beta_const)
     s0 = None
     if w.state_std > 0:
         s0 = torch.randn((len(lens), H, dk, dv), generator=gen, device=device,

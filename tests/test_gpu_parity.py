@@ -2,8 +2,9 @@
 
 Tolerances: bf16 inputs  max|x - x_ref| <= 2e-2 * max|x_ref|, for o and for the
 final state; fp32 inputs 1e-4 on the same measure.  Full-size workloads are
-checked on sampled heads (every token of those heads, every sequence), which
-the oracle computes one (sequence, head) at a time.
+checked on every head, every token and every sequence: the GPU runs the whole
+workload in the launch configuration the benchmark times, and the oracle
+follows it one block of heads at a time (host memory stays bounded).
 """
 import numpy as np
 import pytest
@@ -28,6 +29,30 @@ def rel_err(x, ref) -> float:
 
 def report(name, **errs):
     print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+
+
+def run_prefill_streamed(x, chunk, head_block=16):
+    """GPU on the whole input; the oracle over all heads, head_block heads at a
+    time.  Returns the whole-tensor relative errors of o and the final state."""
+    o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                          x["cu_seqlens"], chunk_size=chunk)
+    torch.cuda.synchronize()
+    H = x["q"].shape[1]
+    cu = x["cu_seqlens"].cpu().numpy()
+    num = {"o": 0.0, "s": 0.0}
+    den = {"o": 0.0, "s": 0.0}
+    for h0 in range(0, H, head_block):
+        hs = slice(h0, min(H, h0 + head_block))
+        sub = lambda t: None if t is None else t[:, hs].cpu()
+        o_ref, sf_ref = oracle.forward(sub(x["q"]), sub(x["k"]), sub(x["v"]), sub(x["g"]),
+                                       sub(x["beta"]), sub(x["initial_state"]), cu)
+        for key, got, ref in (("o", o[:, hs], o_ref), ("s", sf[:, hs], sf_ref)):
+            g64 = got.double().cpu().numpy()
+            assert np.isfinite(g64).all(), "non-finite output"
+            num[key] = max(num[key], float(np.abs(g64 - ref).max(initial=0.0)))
+            den[key] = max(den[key], float(np.abs(ref).max(initial=0.0)))
+        del o_ref, sf_ref
+    return num["o"] / max(den["o"], 1e-30), num["s"] / max(den["s"], 1e-30)
 
 
 def run_prefill(x, chunk, heads=None):
@@ -104,23 +129,36 @@ def test_prefill_shapes(dtype, d, lens, H, std):
 @pytest.mark.parametrize("gate", ["no_decay", "max_decay"])
 @pytest.mark.parametrize("bval", [0.0, 1.0])
 def test_prefill_degenerate_gates(gate, bval):
-    """g = 0 (alpha = 1) or g = g_min everywhere; beta all 0 or all 1."""
-    w = inputs.custom(H=2, dk=128, dv=128, seqlens=[150, 40], state_std=0.1)
+    """g = 0 (alpha = 1) or g = g_min everywhere; beta all 0 or all 1.  With
+    the maximal decay and beta = 0 nothing is written and the prefix state
+    decays by e^-5 a token, so the sequences are kept short enough (at most 14
+    tokens: e^-70 of the prefix, far from the fp32 subnormal range) that the
+    reference state is a normal fp32 number and the comparison can fail."""
+    lens = [14, 9, 5] if (gate == "max_decay" and bval == 0.0) else [150, 40]
+    w = inputs.custom(H=2, dk=128, dv=128, seqlens=lens, state_std=0.1)
     x = inputs.prefill_inputs(w, seed=7, device=DEV)
     x["g"].fill_(0.0 if gate == "no_decay" else -5.0)
     x["beta"].fill_(bval)
-    eo, es = run_prefill(x, 64)
+    o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                          x["cu_seqlens"])
+    torch.cuda.synchronize()
+    cpu = lambda t: t.cpu()
+    o_ref, sf_ref = oracle.forward(*(cpu(x[n]) for n in ("q", "k", "v", "g", "beta",
+                                                         "initial_state")),
+                                   x["cu_seqlens"].cpu().numpy())
+    assert np.abs(sf_ref).max() > 1e-30 and np.abs(o_ref).max() > 1e-30
+    eo, es = rel_err(o, o_ref), rel_err(sf, sf_ref)
     report(f"prefill gate={gate} beta={bval}", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads, sampled heads
+# full-size workloads
 def test_prefill_k3_8k():
     w = inputs.WORKLOADS["k3_prefill_8k"]
     x = inputs.prefill_inputs(w, seed=2, device=DEV)
-    eo, es = run_prefill(x, w.chunk, heads=[0, 31, 64, 95])
-    report("prefill k3 8k", o=eo, state=es)
+    eo, es = run_prefill_streamed(x, w.chunk, head_block=48)
+    report("prefill k3 8k, all 96 heads", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
 
 
@@ -157,8 +195,8 @@ def test_prefill_chunk_128_equals_chunk_64_and_oracle():
 def test_prefill_k3_128k():
     w = inputs.WORKLOADS["k3_prefill_128k"]
     x = inputs.prefill_inputs(w, seed=3, device=DEV)
-    eo, es = run_prefill(x, w.chunk, heads=[0, 95])
-    report("prefill k3 128k (C=128)", o=eo, state=es)
+    eo, es = run_prefill_streamed(x, w.chunk, head_block=16)
+    report("prefill k3 128k (C=128), all 96 heads", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
 
 
@@ -166,8 +204,8 @@ def test_prefill_varlen_prefix():
     w = inputs.WORKLOADS["k3_varlen_prefix"]
     x = inputs.prefill_inputs(w, seed=4, device=DEV)
     print(f"[parity] varlen lengths {x['seqlens']}", flush=True)
-    eo, es = run_prefill(x, w.chunk, heads=[0, 47, 48, 95])
-    report("prefill varlen+prefix", o=eo, state=es)
+    eo, es = run_prefill_streamed(x, w.chunk, head_block=16)
+    report("prefill varlen+prefix, all 96 heads", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
 
 
