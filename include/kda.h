@@ -23,8 +23,9 @@
  *     and every state are always fp32.
  *   - Every pointer except the host-side sizes is a DEVICE pointer and must be
  *     16-byte aligned.
- *   - Supported sizes: d_k == d_v in {32, 64, 128} (bf16) or {32, 64} (fp32
- *     prefill; decode takes all three); chunk_size in {64, 128}.
+ *   - Supported sizes: d_k == d_v in {32, 64, 128}; chunk_size in {64, 128}
+ *     (fp32 prefill with chunk_size 128 stops at d = 64: its 128 x 128 fp32
+ *     tiles do not fit in the 160 KB of LDS a workgroup may use).
  *   - The caller owns every buffer.  The library never allocates, frees or
  *     synchronises: work is enqueued on `stream` and the call returns at once.
  *     Buffers must stay alive until the stream has passed the work.
@@ -64,12 +65,43 @@ typedef int32_t kda_status;
 #define KDA_ERR_HIP 6         /* the HIP runtime reported an error at launch    */
 
 /*
+ * Prefill algorithms (both evaluate the same chunkwise form, "Glossaire",
+ * entries "Chunkwise" and "UT"; they differ in where the intra-chunk work runs):
+ *   KDA_ALGO_FUSED     one persistent kernel per (sequence, head, value slice)
+ *                      forms every intra-chunk quantity on chip, one chunk
+ *                      ahead of the state pass, in 64-token chunks; no
+ *                      workspace.  C = 64 only (bf16 at every head size, fp32
+ *                      up to d = 64).
+ *   KDA_ALGO_TWO_PASS  a chunk-parallel intra pass writes, for every (chunk,
+ *                      head), the operands of the state pass (K o e^G, Q o e^G,
+ *                      (K o e^{G_n - G})^T, (I + A)^-1 Diag(beta), the masked
+ *                      intra attention and the chunk decay) to the workspace;
+ *                      a persistent state pass then walks the chunks in
+ *                      order.  C = 64 or 128 (the chunk the state advances by).
+ *   KDA_ALGO_AUTO      KDA_ALGO_FUSED where it applies, else KDA_ALGO_TWO_PASS.
+ */
+typedef int32_t kda_algo;
+#define KDA_ALGO_AUTO 0
+#define KDA_ALGO_FUSED 1
+#define KDA_ALGO_TWO_PASS 2
+
+/*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (0 means the
- * workspace pointer may be NULL).  Pure host function.
+ * workspace pointer may be NULL).  Pure host function; 0 for unsupported
+ * arguments.  kda_chunk_fwd_algo_workspace_size is the same for a given
+ * algorithm: 0 for KDA_ALGO_FUSED, and for KDA_ALGO_TWO_PASS
+ *     (ceil(total_tokens / C) + num_seqs) * H * P bytes,
+ * P the size of one (chunk, head) packet: 3 C d + m * 256 * (C/16) (C/16 + 1) / 2
+ * elements of the input type (m = 3 for bf16, 2 for fp32) plus 4 d bytes,
+ * rounded up to 256 bytes (bf16, d = 128: 65,024 B at C = 64, 154,112 B at
+ * C = 128).
  */
 size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H,
                                     int32_t d_k, int32_t d_v, int32_t chunk_size,
                                     kda_dtype dtype);
+size_t kda_chunk_fwd_algo_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                         int32_t d_k, int32_t d_v, int32_t chunk_size,
+                                         kda_dtype dtype, kda_algo algo);
 
 /*
  * Chunkwise prefill over packed variable-length sequences.
@@ -89,9 +121,10 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  *                 num_seqs sequences of equal length total_tokens / num_seqs
  *                 (total_tokens must then be a multiple of num_seqs).
  *                 The host never reads cu_seqlens.
- *   chunk_size    64 or 128 (table "Dimensions du modele", row C).  The chunkwise
- *                 form is exact for any block size; this implementation advances
- *                 the state every 64 tokens for both values.
+ *   chunk_size    64 or 128 (table "Dimensions du modele", row C): the block the
+ *                 state advances by.  The chunkwise form is exact for any block
+ *                 size, so results differ between the two only by rounding.
+ *                 kda_chunk_fwd runs KDA_ALGO_AUTO (see kda_chunk_fwd_algo).
  *   o             [total_tokens][H][d_v]  dtype         o_t = S_t^T q_t; must not
  *                                                       alias an input.  May be
  *                                                       NULL when final_state is
@@ -104,7 +137,9 @@ size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int3
  *   and o = NULL the final state is then the transition product of each
  *   sequence ("Glossaire", entry "KCP": the segment summary M).
  *   workspace     device scratch of at least kda_chunk_fwd_workspace_size(...)
- *                 bytes (may be NULL when that size is 0).
+ *                 bytes (may be NULL when that size is 0), else
+ *                 KDA_ERR_WORKSPACE.  Its contents on entry do not matter; it
+ *                 is overwritten.
  * Limits: H * d_k * 4 < 2^24 (one token's fp32 g row below 16 MiB), else
  * KDA_ERR_SHAPE.
  */
@@ -134,6 +169,21 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const f
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_ex with the algorithm chosen by the caller (kda_algo above).
+ * The workspace must hold kda_chunk_fwd_algo_workspace_size(..., algo) bytes.
+ * An algorithm that does not take these sizes, types or chunk size returns
+ * KDA_ERR_UNSUPPORTED.  kda_chunk_fwd_ex(...) is kda_chunk_fwd_algo(...,
+ * KDA_ALGO_AUTO, ...).  The two-pass path enqueues two kernels on `stream`.
+ */
+kda_status kda_chunk_fwd_algo(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *initial_state,
+                              const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                              int32_t H, int32_t d_k, int32_t d_v, int32_t chunk_size,
+                              kda_dtype dtype, kda_dtype o_dtype, kda_algo algo, void *o,
+                              float *final_state, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * One decode step: each of N requests appends one token and advances its own
  * state in place ("Glossaire", entry "Decode": bandwidth bound).
  *
@@ -161,8 +211,9 @@ kda_status kda_step_decode(const void *q, const void *k, const void *v, const fl
  *   A_log         [H]        fp32                  per-head log scale A_h
  *   b_alpha       [H][d_k]   fp32                  per-head decay bias
  * All other arguments, the layouts, sizes, ownership, aliasing and errors are
- * those of kda_chunk_fwd.  The g stream shrinks from 4 to 2 bytes per element
- * (bf16 logits), and no separate normalisation pass is needed.
+ * those of kda_chunk_fwd; this call runs KDA_ALGO_FUSED, so chunk_size must
+ * be 64.  The g stream shrinks from 4 to 2 bytes per element (bf16 logits),
+ * and no separate normalisation pass is needed.
  */
 kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void *v, const void *z,
                                const float *A_log, const float *b_alpha, const float *beta,

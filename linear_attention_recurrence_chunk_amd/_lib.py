@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+# prefill algorithms (kda_algo)
+ALGOS = {"auto": 0, "fused": 1, "two_pass": 2}
 _lib = None
 
 
@@ -48,6 +50,11 @@ def library() -> ctypes.CDLL:
     lib.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                      i32, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd_ex.restype = i32
+    lib.kda_chunk_fwd_algo_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
+    lib.kda_chunk_fwd_algo_workspace_size.restype = sz
+    lib.kda_chunk_fwd_algo.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                       i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_algo.restype = i32
     lib.kda_step_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_step_decode.restype = i32
     lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
@@ -113,9 +120,11 @@ def _out(out: Optional[torch.Tensor], shape, dtype, dev, name: str = "out") -> t
 
 
 def workspace_size(num_seqs: int, total_tokens: int, H: int, d: int, chunk_size: int,
-                   dtype: torch.dtype) -> int:
-    return int(library().kda_chunk_fwd_workspace_size(num_seqs, total_tokens, H, d, d,
-                                                      chunk_size, _DTYPES[dtype]))
+                   dtype: torch.dtype, algo: str = "auto") -> int:
+    if algo not in ALGOS:
+        raise ValueError(f"algo must be one of {sorted(ALGOS)}, got {algo!r}")
+    return int(library().kda_chunk_fwd_algo_workspace_size(num_seqs, total_tokens, H, d, d,
+                                                           chunk_size, _DTYPES[dtype], ALGOS[algo]))
 
 
 def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tensor],
@@ -123,9 +132,10 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None, output: bool = True,
-              o_dtype: Optional[torch.dtype] = None
+              o_dtype: Optional[torch.dtype] = None, algo: str = "auto",
+              workspace: Optional[torch.Tensor] = None
               ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
-    """Chunkwise KDA prefill (kda_chunk_fwd; kda_chunk_fwd_ex for o_dtype).
+    """Chunkwise KDA prefill (kda_chunk_fwd_algo).
 
     q, k [N_tok, H, d_k] or [B, T, H, d_k]; v like q with d_v; g like q (fp32);
     beta [N_tok, H] or [B, T, H] (fp32); initial_state [N, H, d_k, d_v] fp32 or
@@ -135,12 +145,16 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
 
     output=False computes only the final states (o is None and q may be None);
     v=None stands for zero values (d_v = d_k).  o_dtype=torch.float32 with bf16
-    inputs writes o in fp32 (None: the input dtype).
+    inputs writes o in fp32 (None: the input dtype).  algo is "auto", "fused"
+    or "two_pass" (kda_algo); the two-pass path's workspace is allocated here
+    unless a large enough uint8 ``workspace`` tensor is given.
     """
     if not output and not output_final_state and final_state is None:
         raise ValueError("nothing to compute: output=False needs the final state")
     if output and q is None:
         raise ValueError("q is required when the output is computed")
+    if algo not in ALGOS:
+        raise ValueError(f"algo must be one of {sorted(ALGOS)}, got {algo!r}")
     if k.dtype not in _DTYPES:
         raise ValueError(f"k must be bf16 or fp32, got {k.dtype}")
     dev = k.device
@@ -182,21 +196,20 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
     out = _out(out, k.shape[:-1] + (dv,), odt, dev) if output else None
     if final_state is not None or output_final_state:
         final_state = _out(final_state, sshape, torch.float32, dev, "final_state")
-    ws_bytes = workspace_size(num_seqs, n_tok, H, dk, chunk_size, k.dtype)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    lib = library()
-    if odt == k.dtype:
-        st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                               _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv, chunk_size,
-                               _DTYPES[k.dtype], _ptr(out), _ptr(final_state), _ptr(ws), ws_bytes,
-                               _stream(dev))
-        _check("kda_chunk_fwd", st)
+    ws_bytes = workspace_size(num_seqs, n_tok, H, dk, chunk_size, k.dtype, algo)
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=(1,), device=dev)
+        if workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace must hold {ws_bytes} bytes, got {workspace.numel()}")
+        ws, ws_bytes = workspace, workspace.numel()
     else:
-        st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(initial_state), _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv,
-                                  chunk_size, _DTYPES[k.dtype], _DTYPES[odt], _ptr(out),
-                                  _ptr(final_state), _ptr(ws), ws_bytes, _stream(dev))
-        _check("kda_chunk_fwd_ex", st)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = library().kda_chunk_fwd_algo(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(initial_state), _ptr(cu_seqlens), num_seqs, n_tok, H,
+                                      dk, dv, chunk_size, _DTYPES[k.dtype], _DTYPES[odt],
+                                      ALGOS[algo], _ptr(out), _ptr(final_state), _ptr(ws),
+                                      ws_bytes, _stream(dev))
+    _check("kda_chunk_fwd_algo", st)
     return out, final_state
 
 

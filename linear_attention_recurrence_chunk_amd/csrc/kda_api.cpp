@@ -10,6 +10,12 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, const flo
                           const float *beta, const float *s0, const int32_t *cu, int num_seqs,
                           int64_t seq_len, int H, int d, int chunk, bool is_bf16, void *o,
                           bool o_f32, float *sf, hipStream_t stream);
+hipError_t launch_chunked(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *s0, const int32_t *cu, int num_seqs,
+                          int64_t seq_len, int64_t total_tokens, int H, int d, int chunk,
+                          bool is_bf16, void *o, bool o_f32, float *sf, void *ws,
+                          hipStream_t stream);
+size_t chunked_packet_bytes(int d, int chunk, bool is_bf16);
 hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
                                 const void *z, const float *A_log, const float *b_alpha,
                                 const float *beta, const float *s0, const int32_t *cu,
@@ -32,32 +38,53 @@ namespace {
 
 bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-bool head_size_ok(int32_t d, kda_dtype dt, bool prefill)
+bool head_size_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
+
+bool chunk_ok(int32_t c) { return c == 64 || c == 128; }
+
+// Which prefill algorithm runs (KDA_ALGO_AUTO resolved), or -1 when the
+// combination is not supported.  The fused kernel advances the state every
+// 64 tokens and keeps everything on chip; it takes bf16 at every head size and
+// fp32 up to d = 64.  The two-pass path takes both block sizes of the notation
+// table; its fp32 tiles of 128 x 128 do not fit in LDS, so fp32 with C = 128
+// stops at d = 64.
+int resolve_algo(kda_algo algo, int32_t d, int32_t chunk, kda_dtype dt)
 {
-    if (dt == KDA_BF16) return d == 32 || d == 64 || d == 128;
-    if (dt == KDA_F32) return prefill ? (d == 32 || d == 64) : (d == 32 || d == 64 || d == 128);
-    return false;
+    const bool fused_ok = chunk == 64 && (dt == KDA_BF16 || d <= 64);
+    const bool two_ok = dt == KDA_BF16 || chunk == 64 || d <= 64;
+    switch (algo) {
+        case KDA_ALGO_AUTO: return fused_ok ? KDA_ALGO_FUSED : (two_ok ? KDA_ALGO_TWO_PASS : -1);
+        case KDA_ALGO_FUSED: return fused_ok ? KDA_ALGO_FUSED : -1;
+        case KDA_ALGO_TWO_PASS: return two_ok ? KDA_ALGO_TWO_PASS : -1;
+        default: return -1;
+    }
 }
 
-// Both block sizes of the notation table are accepted.  The kernel advances
-// the state every 64 tokens for either value: the chunkwise form is exact for
-// any block size, so the result is the same up to rounding, and on this
-// design a 128-token intra-chunk block only adds work per token.
-bool chunk_ok(int32_t c) { return c == 64 || c == 128; }
+size_t workspace_bytes_for(int alg, int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d,
+                           int32_t chunk, kda_dtype dt)
+{
+    if (alg != KDA_ALGO_TWO_PASS || num_seqs <= 0 || H <= 0) return 0;
+    // one packet per (chunk slot, head); slots stay below ceil(total / C) + num_seqs
+    const int64_t slots = (total_tokens + chunk - 1) / chunk + num_seqs;
+    return (size_t)slots * (size_t)H * kda::chunked_packet_bytes(d, chunk, dt == KDA_BF16);
+}
 
 kda_status prefill_check(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, const float *s0, const int32_t *cu,
                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
-                         int32_t d_v, int32_t chunk, kda_dtype dt, const void *o,
+                         int32_t d_v, int32_t chunk, kda_dtype dt, kda_algo algo, const void *o,
                          const float *sf, const void *ws, size_t ws_bytes, bool optional_io)
 {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || total_tokens < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
-    if (d_k != d_v || !head_size_ok(d_k, dt, true)) return KDA_ERR_UNSUPPORTED;
+    if (d_k != d_v || !head_size_ok(d_k)) return KDA_ERR_UNSUPPORTED;
     if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const int alg = resolve_algo(algo, d_k, chunk, dt);
+    if (alg < 0) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_SHAPE;
     if (!cu && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_SHAPE;
-    if ((int64_t)num_seqs * H * 2 > INT32_MAX) return KDA_ERR_SHAPE;
+    // grid of the state pass: up to 8 value slices per (sequence, head)
+    if ((int64_t)num_seqs * H * 8 > INT32_MAX) return KDA_ERR_SHAPE;
     // the kernel forms row offsets as 24-bit products: one token's fp32 g row
     // (H d_k 4 bytes) must stay below 2^24 bytes
     if ((int64_t)H * d_k * 4 >= ((int64_t)1 << 24)) return KDA_ERR_SHAPE;
@@ -74,8 +101,7 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
         misaligned(s0) || misaligned(cu) || misaligned(o) || misaligned(sf) || misaligned(ws))
         return KDA_ERR_ALIGN;
-    const size_t need =
-        kda_chunk_fwd_workspace_size(num_seqs, total_tokens, H, d_k, d_v, chunk, dt);
+    const size_t need = workspace_bytes_for(alg, num_seqs, total_tokens, H, d_k, chunk, dt);
     if (ws_bytes < need || (need > 0 && !ws)) return KDA_ERR_WORKSPACE;
     return KDA_OK;
 }
@@ -84,10 +110,50 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
 
 extern "C" {
 
-size_t kda_chunk_fwd_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t, int32_t,
-                                    kda_dtype)
+size_t kda_chunk_fwd_algo_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                         int32_t d_k, int32_t d_v, int32_t chunk_size,
+                                         kda_dtype dtype, kda_algo algo)
 {
-    return 0;  // the fused kernel keeps every intermediate on chip
+    if (num_seqs < 0 || total_tokens < 0 || H < 1 || d_k != d_v || !head_size_ok(d_k) ||
+        !chunk_ok(chunk_size) || (dtype != KDA_F32 && dtype != KDA_BF16))
+        return 0;
+    const int alg = resolve_algo(algo, d_k, chunk_size, dtype);
+    return alg < 0 ? 0 : workspace_bytes_for(alg, num_seqs, total_tokens, H, d_k, chunk_size, dtype);
+}
+
+size_t kda_chunk_fwd_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                    int32_t d_k, int32_t d_v, int32_t chunk_size, kda_dtype dtype)
+{
+    return kda_chunk_fwd_algo_workspace_size(num_seqs, total_tokens, H, d_k, d_v, chunk_size,
+                                             dtype, KDA_ALGO_AUTO);
+}
+
+kda_status kda_chunk_fwd_algo(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const float *initial_state,
+                              const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                              int32_t H, int32_t d_k, int32_t d_v, int32_t chunk_size,
+                              kda_dtype dtype, kda_dtype o_dtype, kda_algo algo, void *o,
+                              float *final_state, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    const kda_status st =
+        prefill_check(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, H,
+                      d_k, d_v, chunk_size, dtype, algo, o, final_state, workspace,
+                      workspace_bytes, true);
+    if (st != KDA_OK) return st;
+    if (o_dtype != dtype && o_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return KDA_OK;
+    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
+    const int alg = resolve_algo(algo, d_k, chunk_size, dtype);
+    const hipError_t e =
+        alg == KDA_ALGO_FUSED
+            ? kda::launch_prefill(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, seq_len,
+                                  H, d_k, 64, dtype == KDA_BF16, o, o_dtype == KDA_F32,
+                                  final_state, stream)
+            : kda::launch_chunked(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, seq_len,
+                                  total_tokens, H, d_k, chunk_size, dtype == KDA_BF16, o,
+                                  o_dtype == KDA_F32, final_state, workspace, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
@@ -97,17 +163,9 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const f
                             kda_dtype dtype, kda_dtype o_dtype, void *o, float *final_state,
                             void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    const kda_status st =
-        prefill_check(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, H,
-                      d_k, d_v, chunk_size, dtype, o, final_state, workspace, workspace_bytes, true);
-    if (st != KDA_OK) return st;
-    if (o_dtype != dtype && o_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
-    if (num_seqs == 0) return KDA_OK;
-    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
-    const hipError_t e = kda::launch_prefill(q, k, v, g, beta, initial_state, cu_seqlens,
-                                             num_seqs, seq_len, H, d_k, 64, dtype == KDA_BF16, o,
-                                             o_dtype == KDA_F32, final_state, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return kda_chunk_fwd_algo(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens,
+                              H, d_k, d_v, chunk_size, dtype, o_dtype, KDA_ALGO_AUTO, o,
+                              final_state, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
@@ -133,8 +191,8 @@ kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void 
     // z stands in for g in the common checks (same shape and alignment rule)
     const kda_status st =
         prefill_check(q_raw, k_raw, v, reinterpret_cast<const float *>(z), beta, initial_state,
-                      cu_seqlens, num_seqs, total_tokens, H, d_k, d_v, chunk_size, dtype, o,
-                      final_state, workspace, workspace_bytes, false);
+                      cu_seqlens, num_seqs, total_tokens, H, d_k, d_v, chunk_size, dtype,
+                      KDA_ALGO_FUSED, o, final_state, workspace, workspace_bytes, false);
     if (st != KDA_OK) return st;
     if (total_tokens > 0 && (!A_log || !b_alpha)) return KDA_ERR_NULL;
     if (misaligned(A_log) || misaligned(b_alpha)) return KDA_ERR_ALIGN;
@@ -217,7 +275,7 @@ kda_status kda_step_decode(const void *q, const void *k, const void *v, const fl
 {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
-    if (d_k != d_v || !head_size_ok(d_k, dtype, false)) return KDA_ERR_UNSUPPORTED;
+    if (d_k != d_v || !head_size_ok(d_k)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;

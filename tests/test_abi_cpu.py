@@ -31,7 +31,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert names == sorted(["kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_step_decode",
                             "kda_status_string", "kda_version", "kda_chunk_fwd_fused",
                             "kda_output_gate", "kda_short_conv", "kda_state_compose",
-                            "kda_chunk_fwd_ex", "kda_output_gate_ex"])
+                            "kda_chunk_fwd_ex", "kda_output_gate_ex", "kda_chunk_fwd_algo",
+                            "kda_chunk_fwd_algo_workspace_size"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -44,8 +45,41 @@ def test_version_and_status_strings():
     assert lib.kda_status_string(99) == b"unknown status"
 
 
-def test_workspace_size_is_zero_for_fused_kernel():
-    assert _lib.library().kda_chunk_fwd_workspace_size(16, 100000, 96, 128, 128, 64, 1) == 0
+AUTO, FUSED, TWO_PASS = 0, 1, 2
+
+
+def _packet_bytes(d, C, esize):
+    # Kg, Qg, Kbar^T (C d each), T diag(beta) (two bf16 halves for bf16) and P as
+    # C/16 (C/16 + 1) / 2 blocks of 16 x 16, then gamma (d fp32), rounded up to 256 bytes
+    nb = C // 16
+    nsets = 3 if esize == 2 else 2
+    raw = (3 * C * d + nsets * 256 * nb * (nb + 1) // 2) * esize + 4 * d
+    return (raw + 255) // 256 * 256
+
+
+def test_workspace_sizes():
+    lib = _lib.library()
+    ws = lib.kda_chunk_fwd_workspace_size
+    wsa = lib.kda_chunk_fwd_algo_workspace_size
+    # the fused kernel keeps every intermediate on chip
+    assert ws(16, 100000, 96, 128, 128, 64, 1) == 0
+    assert wsa(16, 100000, 96, 128, 128, 64, 1, FUSED) == 0
+    # two-pass: one packet per (chunk slot, head), slots < ceil(T / C) + N
+    assert _packet_bytes(128, 64, 2) == 65024 and _packet_bytes(128, 128, 2) == 154112
+    for (N, T, H, d, C, dt, es) in [(1, 8192, 96, 128, 64, 1, 2), (16, 135168, 96, 128, 64, 1, 2),
+                                    (1, 131072, 96, 128, 128, 1, 2), (3, 1000, 2, 32, 128, 0, 4),
+                                    (2, 777, 4, 128, 64, 0, 4), (5, 0, 3, 64, 64, 1, 2)]:
+        want = ((T + C - 1) // C + N) * H * _packet_bytes(d, C, es)
+        assert wsa(N, T, H, d, d, C, dt, TWO_PASS) == want
+    # AUTO: the fused kernel where it applies (C = 64, not fp32 at d = 128)
+    assert ws(1, 131072, 96, 128, 128, 128, 1) == wsa(1, 131072, 96, 128, 128, 128, 1, TWO_PASS) > 0
+    assert ws(2, 777, 4, 128, 128, 64, 0) == wsa(2, 777, 4, 128, 128, 64, 0, TWO_PASS) > 0
+    assert ws(2, 777, 4, 64, 64, 64, 0) == 0
+    # unsupported: fp32 with C = 128 at d = 128, the fused kernel with C = 128, bad algo
+    assert wsa(1, 1000, 2, 128, 128, 128, 0, TWO_PASS) == 0
+    assert ws(1, 1000, 2, 128, 128, 128, 0) == 0
+    assert wsa(1, 1000, 2, 64, 64, 128, 1, FUSED) == 0
+    assert wsa(1, 1000, 2, 64, 64, 64, 1, 9) == 0
 
 
 gpu_visible = pytest.mark.skipif(
@@ -87,7 +121,11 @@ def _dec(**kw):
     (dict(num_seqs=0, total=5), ESHAPE),
     (dict(dk=48, dv=48), EUNSUP), (dict(dk=64, dv=128), EUNSUP), (dict(dk=256, dv=256), EUNSUP),
     (dict(chunk=32), EUNSUP), (dict(chunk=96), EUNSUP), (dict(chunk=256), EUNSUP), (dict(dt=7), EUNSUP),
-    (dict(dt=0, dk=128, dv=128), EUNSUP),            # fp32 path is for d <= 64
+    (dict(dt=0, dk=128, dv=128, chunk=128), EUNSUP), # fp32 with C = 128 stops at d = 64
+    (dict(chunk=128), EWS),                          # the two-pass path needs a workspace
+    (dict(chunk=128, ws=A, ws_bytes=1000), EWS),
+    (dict(dt=0, dk=128, dv=128), EWS),               # fp32 at d = 128 runs the two-pass path
+    (dict(chunk=128, ws=MIS, ws_bytes=1 << 30), EALIGN),
     (dict(H=32768, dk=128, dv=128), ESHAPE),         # a token's g row must stay below 16 MiB
     (dict(q=MIS), EALIGN), (dict(g=MIS), EALIGN), (dict(o=MIS), EALIGN),
     (dict(s0=MIS), EALIGN), (dict(sf=MIS), EALIGN), (dict(cu=MIS), EALIGN),
@@ -110,6 +148,28 @@ def _fwd_ex(o_dt, **kw):
         p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]), p(a["cu"]),
         a["num_seqs"], a["total"], a["H"], a["dk"], a["dv"], a["chunk"], a["dt"], o_dt, p(a["o"]),
         p(a["sf"]), p(a["ws"]), a["ws_bytes"], None)
+
+
+def _fwd_algo(algo, **kw):
+    a = dict(q=A, k=A, v=A, g=A, beta=A, s0=None, cu=None, num_seqs=1, total=128, H=2,
+             dk=64, dv=64, chunk=64, dt=1, odt=1, o=A, sf=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _lib.library().kda_chunk_fwd_algo(
+        p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]), p(a["cu"]),
+        a["num_seqs"], a["total"], a["H"], a["dk"], a["dv"], a["chunk"], a["dt"], a["odt"], algo,
+        p(a["o"]), p(a["sf"]), p(a["ws"]), a["ws_bytes"], None)
+
+
+@gpu_visible
+def test_chunk_fwd_algo_rejects():
+    assert _fwd_algo(FUSED, chunk=128) == EUNSUP            # the fused kernel is C = 64
+    assert _fwd_algo(FUSED, dt=0, odt=0, dk=128, dv=128) == EUNSUP
+    assert _fwd_algo(9) == EUNSUP
+    assert _fwd_algo(TWO_PASS) == EWS                        # no workspace
+    assert _fwd_algo(TWO_PASS, ws=A, ws_bytes=10) == EWS
+    assert _fwd_algo(TWO_PASS, num_seqs=0, total=0) == OK    # empty batch: nothing to do
+    assert _fwd_algo(FUSED, num_seqs=0, total=0) == OK
 
 
 @gpu_visible
@@ -173,6 +233,7 @@ def _fused(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(z=None), ENULL), (dict(Al=None), ENULL), (dict(b=None), ENULL), (dict(q=None), ENULL),
     (dict(dk=48, dv=48), EUNSUP), (dict(chunk=32), EUNSUP), (dict(num_seqs=3), ESHAPE),
+    (dict(chunk=128), EUNSUP),                       # the fused front end runs the C = 64 kernel
     (dict(z=MIS), EALIGN), (dict(Al=MIS), EALIGN), (dict(b=MIS), EALIGN),
 ])
 def test_chunk_fwd_fused_rejects(kw, status):

@@ -31,34 +31,52 @@ def report(name, **errs):
     print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
 
 
-def run_prefill_streamed(x, chunk, head_block=16):
-    """GPU on the whole input; the oracle over all heads, head_block heads at a
-    time.  Returns the whole-tensor relative errors of o and the final state."""
-    o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
-                          x["cu_seqlens"], chunk_size=chunk)
+# prefill algorithms of kda_chunk_fwd_algo: the fused kernel (C = 64) and the
+# two-pass path (chunk-parallel intra pass + state pass, C = 64 or 128)
+ALGOS = ["fused", "two_pass"]
+
+
+def algo_ok(algo, dtype, d, chunk):
+    if algo == "fused":
+        return chunk == 64 and (dtype == torch.bfloat16 or d <= 64)
+    return dtype == torch.bfloat16 or chunk == 64 or d <= 64
+
+
+def run_prefill_streamed(x, chunk, head_block=16, algos=("auto",)):
+    """GPU on the whole input (once per algorithm); the oracle over all heads,
+    head_block heads at a time.  Returns {algo: (o error, state error)}, whole-
+    tensor relative errors."""
+    outs = {}
+    for a in algos:
+        outs[a] = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                                x["cu_seqlens"], chunk_size=chunk, algo=a)
     torch.cuda.synchronize()
     H = x["q"].shape[1]
     cu = x["cu_seqlens"].cpu().numpy()
-    num = {"o": 0.0, "s": 0.0}
+    num = {(a, k): 0.0 for a in algos for k in "os"}
     den = {"o": 0.0, "s": 0.0}
     for h0 in range(0, H, head_block):
         hs = slice(h0, min(H, h0 + head_block))
         sub = lambda t: None if t is None else t[:, hs].cpu()
         o_ref, sf_ref = oracle.forward(sub(x["q"]), sub(x["k"]), sub(x["v"]), sub(x["g"]),
                                        sub(x["beta"]), sub(x["initial_state"]), cu)
-        for key, got, ref in (("o", o[:, hs], o_ref), ("s", sf[:, hs], sf_ref)):
-            g64 = got.double().cpu().numpy()
-            assert np.isfinite(g64).all(), "non-finite output"
-            num[key] = max(num[key], float(np.abs(g64 - ref).max(initial=0.0)))
-            den[key] = max(den[key], float(np.abs(ref).max(initial=0.0)))
+        den["o"] = max(den["o"], float(np.abs(o_ref).max(initial=0.0)))
+        den["s"] = max(den["s"], float(np.abs(sf_ref).max(initial=0.0)))
+        for a in algos:
+            o, sf = outs[a]
+            for key, got, ref in (("o", o[:, hs], o_ref), ("s", sf[:, hs], sf_ref)):
+                g64 = got.double().cpu().numpy()
+                assert np.isfinite(g64).all(), f"non-finite output ({a})"
+                num[(a, key)] = max(num[(a, key)], float(np.abs(g64 - ref).max(initial=0.0)))
         del o_ref, sf_ref
-    return num["o"] / max(den["o"], 1e-30), num["s"] / max(den["s"], 1e-30)
+    return {a: (num[(a, "o")] / max(den["o"], 1e-30), num[(a, "s")] / max(den["s"], 1e-30))
+            for a in algos}
 
 
-def run_prefill(x, chunk, heads=None):
+def run_prefill(x, chunk, heads=None, algo="auto"):
     """GPU on the whole input; oracle on `heads` (all when None).  Returns errors."""
     o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
-                          x["cu_seqlens"], chunk_size=chunk)
+                          x["cu_seqlens"], chunk_size=chunk, algo=algo)
     torch.cuda.synchronize()
     hs = slice(None) if heads is None else list(heads)
     sub = lambda t: None if t is None else t[:, hs].cpu()
@@ -98,11 +116,12 @@ def test_decode_k3_256_requests():
 
 # ---------------------------------------------------------------------------
 # prefill, small shapes (whole oracle)
-def test_prefill_tiny_fp32():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_prefill_tiny_fp32(algo):
     w = inputs.WORKLOADS["tiny_fp32"]
     x = inputs.prefill_inputs(w, seed=1, device=DEV)
-    eo, es = run_prefill(x, w.chunk)
-    report("prefill tiny fp32", o=eo, state=es)
+    eo, es = run_prefill(x, w.chunk, algo=algo)
+    report(f"prefill tiny fp32 {algo}", o=eo, state=es)
     assert eo <= 1e-4 and es <= 1e-4
 
 
@@ -114,21 +133,27 @@ CASES = [
     (torch.bfloat16, 32, [333], 2, 0.0),
     (torch.float32, 32, [100, 0, 77, 256], 2, 0.1),
     (torch.float32, 64, [190], 2, 0.1),
+    (torch.float32, 128, [190, 64, 1, 0, 129], 3, 0.1),
 ]
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("dtype,d,lens,H,std", CASES)
-def test_prefill_shapes(dtype, d, lens, H, std):
+def test_prefill_shapes(dtype, d, lens, H, std, algo, chunk):
+    if not algo_ok(algo, dtype, d, chunk):
+        pytest.skip(f"{algo} does not take {dtype} d={d} C={chunk}")
     w = inputs.custom(H=H, dk=d, dv=d, seqlens=lens, dtype=dtype, state_std=std)
     x = inputs.prefill_inputs(w, seed=sum(lens) + d, device=DEV)
-    eo, es = run_prefill(x, 64)
-    report(f"prefill {dtype} d={d} lens={lens}", o=eo, state=es)
+    eo, es = run_prefill(x, chunk, algo=algo)
+    report(f"prefill {algo} C={chunk} {dtype} d={d} lens={lens}", o=eo, state=es)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("algo,chunk", [("fused", 64), ("two_pass", 64), ("two_pass", 128)])
 @pytest.mark.parametrize("gate", ["no_decay", "max_decay"])
 @pytest.mark.parametrize("bval", [0.0, 1.0])
-def test_prefill_degenerate_gates(gate, bval):
+def test_prefill_degenerate_gates(gate, bval, algo, chunk):
     """g = 0 (alpha = 1) or g = g_min everywhere; beta all 0 or all 1.  With
     the maximal decay and beta = 0 nothing is written and the prefix state
     decays by e^-5 a token, so the sequences are kept short enough (at most 14
@@ -140,7 +165,7 @@ def test_prefill_degenerate_gates(gate, bval):
     x["g"].fill_(0.0 if gate == "no_decay" else -5.0)
     x["beta"].fill_(bval)
     o, sf = kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
-                          x["cu_seqlens"])
+                          x["cu_seqlens"], chunk_size=chunk, algo=algo)
     torch.cuda.synchronize()
     cpu = lambda t: t.cpu()
     o_ref, sf_ref = oracle.forward(*(cpu(x[n]) for n in ("q", "k", "v", "g", "beta",
@@ -148,7 +173,7 @@ def test_prefill_degenerate_gates(gate, bval):
                                    x["cu_seqlens"].cpu().numpy())
     assert np.abs(sf_ref).max() > 1e-30 and np.abs(o_ref).max() > 1e-30
     eo, es = rel_err(o, o_ref), rel_err(sf, sf_ref)
-    report(f"prefill gate={gate} beta={bval}", o=eo, state=es)
+    report(f"prefill {algo} C={chunk} gate={gate} beta={bval}", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
 
 
@@ -157,9 +182,10 @@ def test_prefill_degenerate_gates(gate, bval):
 def test_prefill_k3_8k():
     w = inputs.WORKLOADS["k3_prefill_8k"]
     x = inputs.prefill_inputs(w, seed=2, device=DEV)
-    eo, es = run_prefill_streamed(x, w.chunk, head_block=48)
-    report("prefill k3 8k, all 96 heads", o=eo, state=es)
-    assert eo <= 2e-2 and es <= 2e-2
+    errs = run_prefill_streamed(x, w.chunk, head_block=48, algos=ALGOS)
+    for a, (eo, es) in errs.items():
+        report(f"prefill k3 8k {a}, all 96 heads", o=eo, state=es)
+        assert eo <= 2e-2 and es <= 2e-2, a
 
 
 def test_prefill_nano_k3_full_size():
@@ -183,20 +209,21 @@ def test_decode_nano_k3():
     assert eo <= 2e-2 and es <= 2e-2
 
 
-def test_prefill_chunk_128_equals_chunk_64_and_oracle():
+def test_prefill_chunk_128_and_chunk_64_agree_with_oracle():
     w = inputs.custom(H=3, dk=128, dv=128, seqlens=[300, 129], state_std=0.05)
     x = inputs.prefill_inputs(w, seed=17, device=DEV)
-    eo, es = run_prefill(x, 128)
-    report("prefill C=128 small", o=eo, state=es)
-    assert eo <= 2e-2 and es <= 2e-2
+    for chunk in (64, 128):
+        eo, es = run_prefill(x, chunk)
+        report(f"prefill C={chunk} small", o=eo, state=es)
+        assert eo <= 2e-2 and es <= 2e-2
 
 
 @pytest.mark.slow
 def test_prefill_k3_128k():
     w = inputs.WORKLOADS["k3_prefill_128k"]
     x = inputs.prefill_inputs(w, seed=3, device=DEV)
-    eo, es = run_prefill_streamed(x, w.chunk, head_block=16)
-    report("prefill k3 128k (C=128), all 96 heads", o=eo, state=es)
+    (eo, es), = run_prefill_streamed(x, w.chunk, head_block=16).values()
+    report("prefill k3 128k (C=128, two-pass), all 96 heads", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
 
 
@@ -204,9 +231,10 @@ def test_prefill_varlen_prefix():
     w = inputs.WORKLOADS["k3_varlen_prefix"]
     x = inputs.prefill_inputs(w, seed=4, device=DEV)
     print(f"[parity] varlen lengths {x['seqlens']}", flush=True)
-    eo, es = run_prefill_streamed(x, w.chunk, head_block=16)
-    report("prefill varlen+prefix, all 96 heads", o=eo, state=es)
-    assert eo <= 2e-2 and es <= 2e-2
+    errs = run_prefill_streamed(x, w.chunk, head_block=16, algos=ALGOS)
+    for a, (eo, es) in errs.items():
+        report(f"prefill varlen+prefix {a}, all 96 heads", o=eo, state=es)
+        assert eo <= 2e-2 and es <= 2e-2, a
 
 
 # ---------------------------------------------------------------------------
@@ -338,35 +366,42 @@ def _random_cases(n, seed=2024):
     return cases
 
 
+@pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("case", _random_cases(16), ids=lambda c: f"seed{c['seed']}")
-def test_prefill_random_shapes(case):
+def test_prefill_random_shapes(case, algo):
     case = dict(case)
     seed = case.pop("seed")
     w = inputs.custom(**case)
+    chunk = w.chunk if algo == "two_pass" else 64
     x = inputs.prefill_inputs(w, seed=seed, device=DEV)
-    eo, es = run_prefill(x, w.chunk)
-    report(f"prefill random {case}", o=eo, state=es)
+    eo, es = run_prefill(x, chunk, algo=algo)
+    report(f"prefill random {algo} C={chunk} {case}", o=eo, state=es)
     tol = TOL[w.dtype]
     assert eo <= tol and es <= tol
 
 
 # ---------------------------------------------------------------------------
 # state-only calls (o = NULL) and zero values (v = NULL)
+@pytest.mark.parametrize("algo,chunk", [("fused", 64), ("two_pass", 64), ("two_pass", 128)])
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
-                                     (torch.float32, 32), (torch.float32, 64)])
-def test_prefill_state_only(dtype, d):
+                                     (torch.float32, 32), (torch.float32, 64),
+                                     (torch.float32, 128)])
+def test_prefill_state_only(dtype, d, algo, chunk):
+    if not algo_ok(algo, dtype, d, chunk):
+        pytest.skip(f"{algo} does not take {dtype} d={d} C={chunk}")
     w = inputs.custom(H=3, dk=d, dv=d, seqlens=[100, 0, 64, 1, 200], state_std=0.1, dtype=dtype)
     x = inputs.prefill_inputs(w, seed=60 + d, device=DEV)
     args = (x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
-    _, sf_full = kda.chunk_fwd(x["q"], *args)
-    o_none, sf = kda.chunk_fwd(None, *args, output=False)
+    kw = dict(chunk_size=chunk, algo=algo)
+    _, sf_full = kda.chunk_fwd(x["q"], *args, **kw)
+    o_none, sf = kda.chunk_fwd(None, *args, output=False, **kw)
     torch.cuda.synchronize()
     assert o_none is None
     # the state path is the same arithmetic with or without the output
     es_full = rel_err(sf, sf_full.cpu().double().numpy())
     # zero values: the oracle with v = 0
     _, sz = kda.chunk_fwd(None, x["k"], None, x["g"], x["beta"], x["initial_state"],
-                          x["cu_seqlens"], output=False)
+                          x["cu_seqlens"], output=False, **kw)
     torch.cuda.synchronize()
     cpu = lambda t: t.cpu()
     _, sz_ref = oracle.forward(cpu(x["q"]), cpu(x["k"]), torch.zeros_like(cpu(x["v"])),
@@ -376,7 +411,8 @@ def test_prefill_state_only(dtype, d):
                                cpu(x["beta"]), cpu(x["initial_state"]),
                                x["cu_seqlens"].cpu().numpy())
     es, ez = rel_err(sf, sf_ref), rel_err(sz, sz_ref)
-    report(f"prefill state only {dtype} d={d}", vs_full=es_full, state=es, zero_v=ez)
+    report(f"prefill state only {algo} C={chunk} {dtype} d={d}", vs_full=es_full, state=es,
+           zero_v=ez)
     assert es_full <= 1e-6 and es <= TOL[dtype] and ez <= TOL[dtype]
 
 
@@ -401,14 +437,15 @@ def test_binding_rejects_mismatched_outputs():
 
 # ---------------------------------------------------------------------------
 # fp32 attention output from bf16 inputs (kda_chunk_fwd_ex)
+@pytest.mark.parametrize("algo,chunk", [("fused", 64), ("two_pass", 64), ("two_pass", 128)])
 @pytest.mark.parametrize("d", [128, 64, 32])
-def test_prefill_fp32_output(d):
+def test_prefill_fp32_output(d, algo, chunk):
     w = inputs.custom(H=3, dk=d, dv=d, seqlens=[130, 0, 64, 7], state_std=0.05,
                       dtype=torch.bfloat16)
     x = inputs.prefill_inputs(w, seed=90 + d, device=DEV)
     args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"], x["cu_seqlens"])
-    o16, s16 = kda.chunk_fwd(*args)
-    o32, s32 = kda.chunk_fwd(*args, o_dtype=torch.float32)
+    o16, s16 = kda.chunk_fwd(*args, chunk_size=chunk, algo=algo)
+    o32, s32 = kda.chunk_fwd(*args, o_dtype=torch.float32, chunk_size=chunk, algo=algo)
     torch.cuda.synchronize()
     assert o32.dtype == torch.float32 and o16.dtype == torch.bfloat16
     # the same arithmetic up to the store: the bf16 output is the rounded fp32 one,
@@ -418,5 +455,5 @@ def test_prefill_fp32_output(d):
     cpu = lambda t: t.cpu()
     o_ref, s_ref = oracle.forward(*(cpu(t) for t in args[:6]), x["cu_seqlens"].cpu().numpy())
     eo, es = rel_err(o32, o_ref), rel_err(s32, s_ref)
-    report(f"prefill fp32 output d={d}", o=eo, state=es)
+    report(f"prefill fp32 output {algo} C={chunk} d={d}", o=eo, state=es)
     assert eo <= 2e-2 and es <= 2e-2
