@@ -63,6 +63,8 @@ typedef int32_t kda_status;
 #define KDA_ERR_ALIGN 4       /* a pointer is not 16-byte aligned               */
 #define KDA_ERR_WORKSPACE 5   /* workspace smaller than the size asked for      */
 #define KDA_ERR_HIP 6         /* the HIP runtime reported an error at launch    */
+#define KDA_ERR_TOO_LARGE 7   /* sizes exceed the static scratch of the
+                                 no-allocation call                              */
 
 /*
  * Prefill algorithms (both evaluate the same chunkwise form, "Glossaire",
@@ -182,6 +184,32 @@ kda_status kda_chunk_fwd_algo(const void *q, const void *k, const void *v, const
                               kda_dtype dtype, kda_dtype o_dtype, kda_algo algo, void *o,
                               float *final_state, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * The two-pass prefill (KDA_ALGO_TWO_PASS) for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Instead of a caller workspace it uses a static device
+ * buffer of kda_chunk_fwd_static_scratch_bytes() bytes (256 MiB) inside the
+ * library; it calls no hipMalloc, hipFree or allocating library routine.
+ *   - Sizes whose kda_chunk_fwd_algo_workspace_size(..., KDA_ALGO_TWO_PASS)
+ *     exceeds that buffer return KDA_ERR_TOO_LARGE before any HIP call (at
+ *     H = 96, d = 128, bf16, C = 64: about 2,600 tokens of one sequence).
+ *   - Each GPU the library runs on holds one such buffer until the process
+ *     ends.  Every call on a GPU shares it: calls that overlap on one GPU (two
+ *     streams, or two host threads) race and must be serialised by the caller.
+ *     The buffer needs no clearing between calls.
+ *   - Everything else (arguments, layouts, results, errors, o_dtype) is as in
+ *     kda_chunk_fwd_algo with KDA_ALGO_TWO_PASS; results equal that call's
+ *     bit for bit.
+ */
+kda_status kda_chunk_fwd_two_pass_static(const void *q, const void *k, const void *v,
+                                         const float *g, const float *beta,
+                                         const float *initial_state, const int32_t *cu_seqlens,
+                                         int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                         int32_t d_k, int32_t d_v, int32_t chunk_size,
+                                         kda_dtype dtype, kda_dtype o_dtype, void *o,
+                                         float *final_state, hipStream_t stream);
+size_t kda_chunk_fwd_static_scratch_bytes(void);
 
 /*
  * One decode step: each of N requests appends one token and advances its own

@@ -55,6 +55,11 @@ def library() -> ctypes.CDLL:
     lib.kda_chunk_fwd_algo.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                        i32, i32, i32, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd_algo.restype = i32
+    lib.kda_chunk_fwd_two_pass_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                                  i32, i32, i32, i32, vp, vp, vp]
+    lib.kda_chunk_fwd_two_pass_static.restype = i32
+    lib.kda_chunk_fwd_static_scratch_bytes.argtypes = []
+    lib.kda_chunk_fwd_static_scratch_bytes.restype = sz
     lib.kda_step_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_step_decode.restype = i32
     lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
@@ -211,6 +216,44 @@ def chunk_fwd(q: Optional[torch.Tensor], k: torch.Tensor, v: Optional[torch.Tens
                                       ws_bytes, _stream(dev))
     _check("kda_chunk_fwd_algo", st)
     return out, final_state
+
+
+def chunk_fwd_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, initial_state: Optional[torch.Tensor],
+                     cu_seqlens: Optional[torch.Tensor], out: torch.Tensor,
+                     final_state: torch.Tensor, chunk_size: int = 64) -> None:
+    """The two-pass prefill on the library's static scratch
+    (kda_chunk_fwd_two_pass_static): no device allocation here or in the
+    library.  Packed 3-D inputs as chunk_fwd; ``out`` (o, dtype of the inputs or
+    fp32) and ``final_state`` must be preallocated."""
+    if k.dtype not in _DTYPES:
+        raise ValueError(f"k must be bf16 or fp32, got {k.dtype}")
+    dev = k.device
+    _gpu(dev)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, name, dtype=k.dtype, ndim=(3,), device=dev)
+    _need(g, "g", dtype=torch.float32, ndim=(3,), device=dev)
+    _need(beta, "beta", dtype=torch.float32, ndim=(2,), device=dev)
+    num_seqs, n_tok = _layout(k, cu_seqlens)
+    H, dk = k.shape[-2:]
+    dv = v.shape[-1]
+    if q.shape != k.shape or g.shape != k.shape or v.shape[:-1] != k.shape[:-1] or \
+            beta.shape != k.shape[:-1]:
+        raise ValueError("q, k, g must share a shape; v and beta must match it")
+    sshape = (num_seqs, H, dk, dv)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", dtype=torch.float32, device=dev)
+        if tuple(initial_state.shape) != sshape:
+            raise ValueError(f"initial_state must have shape {sshape}")
+    if out.dtype not in (k.dtype, torch.float32):
+        raise ValueError(f"out must be {k.dtype} or torch.float32")
+    _out(out, v.shape, out.dtype, dev)
+    _out(final_state, sshape, torch.float32, dev, "final_state")
+    st = library().kda_chunk_fwd_two_pass_static(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        num_seqs, n_tok, H, dk, dv, chunk_size, _DTYPES[k.dtype], _DTYPES[out.dtype], _ptr(out),
+        _ptr(final_state), _stream(dev))
+    _check("kda_chunk_fwd_two_pass_static", st)
 
 
 def step_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

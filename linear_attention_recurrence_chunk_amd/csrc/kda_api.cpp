@@ -16,6 +16,8 @@ hipError_t launch_chunked(const void *q, const void *k, const void *v, const flo
                           bool is_bf16, void *o, bool o_f32, float *sf, void *ws,
                           hipStream_t stream);
 size_t chunked_packet_bytes(int d, int chunk, bool is_bf16);
+size_t static_scratch_bytes();
+hipError_t static_scratch_ptr(void **ptr);
 hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
                                 const void *z, const float *A_log, const float *b_alpha,
                                 const float *beta, const float *s0, const int32_t *cu,
@@ -73,7 +75,8 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
                          const float *beta, const float *s0, const int32_t *cu,
                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
                          int32_t d_v, int32_t chunk, kda_dtype dt, kda_algo algo, const void *o,
-                         const float *sf, const void *ws, size_t ws_bytes, bool optional_io)
+                         const float *sf, const void *ws, size_t ws_bytes, bool optional_io,
+                         bool check_ws = true)
 {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || total_tokens < 0 || H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
@@ -102,7 +105,7 @@ kda_status prefill_check(const void *q, const void *k, const void *v, const floa
         misaligned(s0) || misaligned(cu) || misaligned(o) || misaligned(sf) || misaligned(ws))
         return KDA_ERR_ALIGN;
     const size_t need = workspace_bytes_for(alg, num_seqs, total_tokens, H, d_k, chunk, dt);
-    if (ws_bytes < need || (need > 0 && !ws)) return KDA_ERR_WORKSPACE;
+    if (check_ws && (ws_bytes < need || (need > 0 && !ws))) return KDA_ERR_WORKSPACE;
     return KDA_OK;
 }
 
@@ -155,6 +158,37 @@ kda_status kda_chunk_fwd_algo(const void *q, const void *k, const void *v, const
                                   o_dtype == KDA_F32, final_state, workspace, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+kda_status kda_chunk_fwd_two_pass_static(const void *q, const void *k, const void *v,
+                                         const float *g, const float *beta,
+                                         const float *initial_state, const int32_t *cu_seqlens,
+                                         int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                         int32_t d_k, int32_t d_v, int32_t chunk_size,
+                                         kda_dtype dtype, kda_dtype o_dtype, void *o,
+                                         float *final_state, hipStream_t stream)
+{
+    // host checks first (workspace checked against the static scratch below)
+    const kda_status st =
+        prefill_check(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, H,
+                      d_k, d_v, chunk_size, dtype, KDA_ALGO_TWO_PASS, o, final_state, nullptr, 0,
+                      true, false);
+    if (st != KDA_OK) return st;
+    if (o_dtype != dtype && o_dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+    const size_t need = workspace_bytes_for(KDA_ALGO_TWO_PASS, num_seqs, total_tokens, H, d_k,
+                                            chunk_size, dtype);
+    if (need > kda::static_scratch_bytes()) return KDA_ERR_TOO_LARGE;
+    if (num_seqs == 0) return KDA_OK;
+    void *ws = nullptr;
+    if (kda::static_scratch_ptr(&ws) != hipSuccess) return KDA_ERR_HIP;
+    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
+    const hipError_t e = kda::launch_chunked(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs,
+                                             seq_len, total_tokens, H, d_k, chunk_size,
+                                             dtype == KDA_BF16, o, o_dtype == KDA_F32, final_state,
+                                             ws, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_chunk_fwd_static_scratch_bytes(void) { return kda::static_scratch_bytes(); }
 
 kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
                             const float *beta, const float *initial_state,
@@ -297,6 +331,7 @@ const char *kda_status_string(kda_status s)
         case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "workspace smaller than kda_chunk_fwd_workspace_size";
         case KDA_ERR_HIP: return "HIP launch error";
+        case KDA_ERR_TOO_LARGE: return "sizes need more than the static scratch of the no-allocation call";
         default: return "unknown status";
     }
 }

@@ -45,6 +45,7 @@
 // the sequence lengths.
 #include "kda_common.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace kda {
@@ -998,6 +999,42 @@ __global__ __launch_bounds__(1024, 1) void state_kernel(
 #undef S
 #undef Zt
 }  // namespace cp
+
+// ---------------------------------------------------------------------------
+// Static scratch of the no-allocation entry point: the two-pass workspace for
+// callers that cannot allocate device memory.  Every GPU the library runs on
+// holds one copy until the process ends; all calls on a GPU share it, so calls
+// that overlap on one GPU race.  Nothing in it has to start at zero: every
+// packet slot the state pass reads is written first by the intra pass of the
+// same call.
+constexpr size_t kStaticScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+// Device address of this device's copy of `scratch` (looked up once per device,
+// with that device current).  In host code the array's name is a host-side
+// stand-in, never a device address.
+hipError_t static_scratch_ptr(void **ptr)
+{
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------
 // Host side

@@ -16,7 +16,7 @@ from linear_attention_recurrence_chunk_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = range(7)
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, ETOOLARGE = range(8)
 
 
 def _declared_functions():
@@ -32,7 +32,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                             "kda_status_string", "kda_version", "kda_chunk_fwd_fused",
                             "kda_output_gate", "kda_short_conv", "kda_state_compose",
                             "kda_chunk_fwd_ex", "kda_output_gate_ex", "kda_chunk_fwd_algo",
-                            "kda_chunk_fwd_algo_workspace_size"])
+                            "kda_chunk_fwd_algo_workspace_size", "kda_chunk_fwd_two_pass_static",
+                            "kda_chunk_fwd_static_scratch_bytes"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -40,8 +41,8 @@ def test_library_loads_and_exports_every_declared_symbol():
 def test_version_and_status_strings():
     lib = _lib.library()
     assert lib.kda_version() == 1
-    for s in range(7):
-        assert lib.kda_status_string(s)
+    for s in range(8):
+        assert lib.kda_status_string(s) != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
 
 
@@ -170,6 +171,33 @@ def test_chunk_fwd_algo_rejects():
     assert _fwd_algo(TWO_PASS, ws=A, ws_bytes=10) == EWS
     assert _fwd_algo(TWO_PASS, num_seqs=0, total=0) == OK    # empty batch: nothing to do
     assert _fwd_algo(FUSED, num_seqs=0, total=0) == OK
+
+
+def _fwd_static(**kw):
+    a = dict(q=A, k=A, v=A, g=A, beta=A, s0=None, cu=None, num_seqs=1, total=128, H=2,
+             dk=64, dv=64, chunk=64, dt=1, odt=1, o=A, sf=None)
+    a.update(kw)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return _lib.library().kda_chunk_fwd_two_pass_static(
+        p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]), p(a["cu"]),
+        a["num_seqs"], a["total"], a["H"], a["dk"], a["dv"], a["chunk"], a["dt"], a["odt"],
+        p(a["o"]), p(a["sf"]), None)
+
+
+def test_static_scratch_size():
+    assert _lib.library().kda_chunk_fwd_static_scratch_bytes() == 256 << 20
+
+
+@gpu_visible
+def test_chunk_fwd_static_rejects():
+    # the common checks, then the static scratch's capacity, all before any HIP call
+    assert _fwd_static(q=None) == ENULL
+    assert _fwd_static(dk=48, dv=48) == EUNSUP
+    assert _fwd_static(dt=0, odt=0, dk=128, dv=128, chunk=128) == EUNSUP
+    assert _fwd_static(o=MIS) == EALIGN
+    assert _fwd_static(odt=7) == EUNSUP
+    assert _fwd_static(total=8192, H=96, dk=128, dv=128) == ETOOLARGE   # 8K x 96 heads
+    assert _fwd_static(num_seqs=0, total=0) == OK
 
 
 @gpu_visible
