@@ -4,18 +4,22 @@
 
 A step is one kda_chunk_fwd over the whole workload (default: one sequence of
 8192 tokens, H = 96, d_k = d_v = 128, C = 64, bf16 q/k/v, fp32 g/beta), with
-every input already resident in HBM.  The decode step (256 requests, H = 96,
-fp32 states updated in place) is timed after it and reported under "decode".
-Rank 0 prints one JSON line.
+every input already resident in HBM, on the default algorithm (KDA_ALGO_AUTO:
+the fused kernel at C = 64).  The decode step (256 requests, H = 96, fp32
+states updated in place) is timed after it and reported under "decode"; the
+two-pass algorithm on the same workload under "two_pass".  Rank 0 prints one
+JSON line.
 
 Roofline figures (per launch):
   prefill bytes  B_alg = N_tok H [e_in (2 d_k + d_v) + 4 d_k + 4 + e_out d_v]
                          + N_seq H d_k d_v 4 (has_initial + has_final)
-  prefill flops  F     = N_tok H [C (3 d_k + 2 d_v) + 6 d_k d_v]
-                 (K K^T, Q K^T, T R, P U at C^2 d / 2 each, triangle-aware, and
-                  K e^G S, Q e^G S, Kbar^T U at 2 C d_k d_v / C each per token)
+  prefill flops  F     = N_tok H [C (2 d_k + 2 d_v) + 6 d_k d_v]
+                 (the four triangular products K K^T, Q K^T, T R and P U, each
+                  C^2 d / 2 multiply-adds a chunk, i.e. C d flops per token,
+                  and the three state products (K o e^G) S, (Q o e^G) S and
+                  Kbar^T U, 2 d_k d_v flops per token each; C is the state step)
   decode bytes   N H [8 d_k d_v + e_in (2 d_k + d_v) + 4 d_k + 4 + e_out d_v]
-The prefill at these shapes is bound by HBM (90 flop per byte, below the
+The prefill at these shapes is bound by HBM (86 flop per byte, below the
 bf16 ridge of 2.5e15 / 8e12 = 312), so the roofline object uses HBM bandwidth;
 the matrix-core fraction is reported beside it.
 """
@@ -35,7 +39,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 METRIC = "KDA prefill tokens/s (H=96, d_k=d_v=128) + % bf16 MFMA peak; decode HBM GB/s"
-EXEC_CHUNK = 64                # tokens per state step of the kernel, for either chunk_size
+
+
+def state_step(algo, chunk):
+    """Tokens the state advances by: the fused kernel always steps 64 tokens
+    (it takes chunk_size 64 only), the two-pass path steps chunk_size."""
+    return 64 if algo in ("auto", "fused") and chunk == 64 else chunk
 
 
 def prefill_bytes(n_tok, n_seq, H, dk, dv, e_in, e_out, has_s0, has_sf):
@@ -44,7 +53,7 @@ def prefill_bytes(n_tok, n_seq, H, dk, dv, e_in, e_out, has_s0, has_sf):
 
 
 def prefill_flops(n_tok, H, dk, dv, C):
-    return n_tok * H * (C * (3 * dk + 2 * dv) + 6 * dk * dv)
+    return n_tok * H * (C * (2 * dk + 2 * dv) + 6 * dk * dv)
 
 
 def decode_bytes(N, H, dk, dv, e_in, e_out):
@@ -64,32 +73,87 @@ def _gbs(nbytes, ms):
 
 def bench_configs(args, torch, kda, inputs, dev):
     """The other workloads of the benchmark table, each timed on its own: the
-    tiny fp32 case, the 131072-token sequence (chunk_size 128) and the 16
-    packed sequences with prefix states."""
+    tiny fp32 case, the 131072-token sequence at chunk_size 128 (the two-pass
+    path, whose state advances 128 tokens a step) and, beside it, the same
+    sequence on the fused kernel's 64-token steps, and the 16 packed sequences
+    with prefix states."""
     res = {}
-    for name, steps in (("tiny_fp32", args.steps), ("k3_prefill_128k", 5), ("k3_varlen_prefix", 5)):
+    for label, name, steps, algo, chunk in (
+            ("tiny_fp32", "tiny_fp32", args.steps, "auto", None),
+            ("k3_prefill_128k", "k3_prefill_128k", 5, "auto", None),
+            ("k3_prefill_128k_fused_c64", "k3_prefill_128k", 5, "fused", 64),
+            ("k3_varlen_prefix", "k3_varlen_prefix", 5, "auto", None)):
         wc = inputs.WORKLOADS[name]
+        C = wc.chunk if chunk is None else chunk
         xc = inputs.prefill_inputs(wc, seed=2, device=dev)
         nt, ns = int(xc["q"].shape[0]), len(xc["seqlens"])
         oc = torch.empty_like(xc["v"])
         sfc = torch.empty((ns, wc.H, wc.dk, wc.dv), dtype=torch.float32, device=dev)
+        wsb = kda.workspace_size(ns, nt, wc.H, wc.dk, C, xc["q"].dtype, algo)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
 
         def cstep():
             kda.chunk_fwd(xc["q"], xc["k"], xc["v"], xc["g"], xc["beta"], xc["initial_state"],
-                          xc["cu_seqlens"], chunk_size=wc.chunk, out=oc, final_state=sfc)
+                          xc["cu_seqlens"], chunk_size=C, out=oc, final_state=sfc, algo=algo,
+                          workspace=ws)
 
         ms, _ = time_launches(cstep, steps, 2, torch)
         e = xc["q"].element_size()
         b = prefill_bytes(nt, ns, wc.H, wc.dk, wc.dv, e, e, xc["initial_state"] is not None, True)
-        f = prefill_flops(nt, wc.H, wc.dk, wc.dv, EXEC_CHUNK)
-        res[name] = {"tokens": nt, "sequences": ns, "H": wc.H, "d": wc.dk, "chunk": wc.chunk,
-                     "ms_per_step": ms, "tokens/s": nt / (ms * 1e-3),
-                     "roofline": {"bound": "hbm", "achieved": _gbs(b, ms), "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": _gbs(b, ms) / HBM_PEAK_GBS,
-                                  "traffic": None, "kernel": "kda::prefill_kernel",
-                                  "bytes_per_launch": b},
-                     "mfma_frac": f / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-        del xc, oc, sfc
+        two = wsb > 0
+        f = prefill_flops(nt, wc.H, wc.dk, wc.dv, state_step(algo, C))
+        res[label] = {"workload": name, "tokens": nt, "sequences": ns, "H": wc.H, "d": wc.dk,
+                      "chunk": C, "state_step": state_step(algo, C),
+                      "algo": "two_pass" if two else "fused", "workspace_bytes": wsb,
+                      "ms_per_step": ms, "tokens/s": nt / (ms * 1e-3),
+                      "roofline": {"bound": "hbm", "achieved": _gbs(b, ms), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": _gbs(b, ms) / HBM_PEAK_GBS,
+                                   "traffic": None,
+                                   "kernel": ("kda::cp::intra_kernel + kda::cp::state_kernel"
+                                              if two else "kda::prefill_kernel"),
+                                   "bytes_per_launch": b},
+                      "mfma_frac": f / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        del xc, oc, sfc, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_two_pass(args, w, x, torch, kda, dev):
+    """The two-pass algorithm (chunk-parallel intra pass, then the state pass)
+    on the headline workload, at chunk_size 64 and 128.  The algorithmic bytes
+    are those of the operation; the packet round trip through the workspace
+    (written by the intra pass, read by the state pass) is reported apart."""
+    res = {}
+    n_tok, n_seq = int(x["q"].shape[0]), len(x["seqlens"])
+    e = x["q"].element_size()
+    o = torch.empty_like(x["v"])
+    sf = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    b = prefill_bytes(n_tok, n_seq, w.H, w.dk, w.dv, e, e, x["initial_state"] is not None, True)
+    for C in (64, 128):
+        wsb = kda.workspace_size(n_seq, n_tok, w.H, w.dk, C, x["q"].dtype, "two_pass")
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def tstep():
+            kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
+                          x["cu_seqlens"], chunk_size=C, out=o, final_state=sf, algo="two_pass",
+                          workspace=ws)
+
+        ms, _ = time_launches(tstep, args.steps, args.warmup, torch)
+        # packets actually used: one per (chunk, head); written once, read by
+        # each of the state pass's value slices (shared through L2)
+        nch = (n_tok + C - 1) // C
+        pk = kda.workspace_size(1, C, 1, w.dk, C, x["q"].dtype, "two_pass") // 2
+        res[f"chunk_{C}"] = {
+            "workload": w.name, "chunk": C, "state_step": C, "ms_per_step": ms,
+            "tokens/s": n_tok / (ms * 1e-3), "workspace_bytes": wsb,
+            "packet_bytes": pk, "packet_round_trip_bytes": 2 * nch * w.H * pk,
+            "roofline": {"bound": "hbm", "achieved": _gbs(b, ms), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": _gbs(b, ms) / HBM_PEAK_GBS,
+                         "traffic": _traffic("kda_chunked.hip", f"{w.name}_two_pass_c{C}"),
+                         "kernel": "kda::cp::intra_kernel + kda::cp::state_kernel",
+                         "bytes_per_launch": b},
+            "mfma_frac": prefill_flops(n_tok, w.H, w.dk, w.dv, C) / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        del ws
         torch.cuda.empty_cache()
     return res
 
@@ -256,6 +320,16 @@ def time_launches(fn, steps, warmup, torch):
     return start.elapsed_time(end) / steps, wall
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(x, w, min_seconds=10.0, max_seconds=30.0):
     """The fp64 oracle on a bounded sample of the workload: the first H'
     heads (every token), threaded over (sequence, head) on all host cores,
@@ -278,7 +352,7 @@ def cpu_baseline(x, w, min_seconds=10.0, max_seconds=30.0):
             break
     # full-workload tokens per second (a token carries all H heads)
     return {"value": reps * n_tok * h / w.H / dt, "unit": "tokens/s",
-            "cores": min(cores, h * (len(cu) - 1)), "kind": "oracle",
+            "cores": min(cores, h * (len(cu) - 1)), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{reps} pass(es) over {h} of {w.H} heads x all {n_tok} tokens of "
                       f"{w.name}, fp64, {dt:.1f} s"}
 
@@ -294,6 +368,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (tiny fp32, 128K tokens, varlen with prefixes)")
+    ap.add_argument("--algo", default="auto", choices=("auto", "fused", "two_pass"),
+                    help="prefill algorithm of the headline measurement")
+    ap.add_argument("--chunk", type=int, default=None, help="chunk_size (default: the workload's)")
+    ap.add_argument("--no-two-pass", action="store_true",
+                    help="skip the two-pass measurements on the headline workload")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the layer steps (fused front end, output gate, ShortConv, "
                          "segment composition) and the nano-K3 shapes")
@@ -318,16 +397,21 @@ def main():
     n_tok, n_seq = int(x["q"].shape[0]), len(x["seqlens"])
     o = torch.empty_like(x["v"])
     sf = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    C = w.chunk if args.chunk is None else args.chunk
+    wsb = kda.workspace_size(n_seq, n_tok, w.H, w.dk, C, x["q"].dtype, args.algo)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    algo_run = "two_pass" if wsb else "fused"
 
     def step():
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["initial_state"],
-                      x["cu_seqlens"], chunk_size=w.chunk, out=o, final_state=sf)
+                      x["cu_seqlens"], chunk_size=C, out=o, final_state=sf, algo=args.algo,
+                      workspace=ws)
 
     ms, wall = time_launches(step, args.steps, args.warmup, torch)
     e = x["q"].element_size()
     bytes_ = prefill_bytes(n_tok, n_seq, w.H, w.dk, w.dv, e, e,
                            x["initial_state"] is not None, True)
-    flops = prefill_flops(n_tok, w.H, w.dk, w.dv, EXEC_CHUNK)
+    flops = prefill_flops(n_tok, w.H, w.dk, w.dv, state_step(algo_run, C))
     gbs = bytes_ / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     toks = n_tok / (ms * 1e-3)
@@ -345,13 +429,16 @@ def main():
         "dtype": "bf16" if x["q"].dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": n_seq, "tokens": n_tok, "H": w.H,
-                   "d_k": w.dk, "d_v": w.dv, "chunk": w.chunk, "state_step": EXEC_CHUNK,
-                   "initial_state": x["initial_state"] is not None,
+                   "d_k": w.dk, "d_v": w.dv, "chunk": C, "state_step": state_step(algo_run, C),
+                   "algo": algo_run, "initial_state": x["initial_state"] is not None,
                    "parallelism": "single_gpu"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": _traffic("kda_prefill.hip", w.name),
-                     "kernel": "kda::prefill_kernel", "bytes_per_launch": bytes_},
+                     "traffic": (_traffic("kda_chunked.hip", f"{w.name}_two_pass_c{C}") if wsb
+                                 else _traffic("kda_prefill.hip", w.name)),
+                     "kernel": ("kda::cp::intra_kernel + kda::cp::state_kernel" if wsb
+                                else "kda::prefill_kernel"),
+                     "bytes_per_launch": bytes_},
         "mfma": {"tflops": tflops, "peak": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
                  "flops_per_launch": flops},
         "wall_s_timed": wall,
@@ -379,6 +466,9 @@ def main():
                                                     "bytes_per_launch": dbytes}}
         del xd
 
+    del ws
+    if not args.no_two_pass:
+        out["two_pass"] = bench_two_pass(args, w, x, torch, kda, dev)
     if not args.no_layer:
         out["layer"] = bench_layer(args, w, x, torch, kda, inputs, dev)
     if not args.no_configs:

@@ -673,6 +673,60 @@ __device__ __forceinline__ int rows_in(int64_t t0, int64_t eos, int C)
     return n < C ? (int)n : C;
 }
 
+// (I + N)^-1 of diagonal block I by recursive block inversion, N = A_II (with
+// beta) given in both layouts.  Let D_b be the block-diagonal matrix of the
+// inverses of the b x b diagonal blocks of I + N, and F_b the part of N that
+// lies in the lower-left b x b block of each 2b x 2b diagonal block.  Then
+// D_2b = D_b - D_b F_b D_b; D_1 = I gives D_2 = I - F_1, and three more levels
+// reach D_16.  Every intermediate is a block of the true inverse, whose entries
+// stay small when the keys of a sub-block are alike (the power-series product
+// (I - N)(I + N^2)(I + N^4)(I + N^8) instead forms powers that grow like
+// binomial coefficients and cancel).  Layouts: a lane's values of X in the A
+// layout (X[n16][4 grp + i]) are those of X^T in the D layout
+// (X[4 grp + i][n16]), so a product X Y comes in the D layout from
+// mma16(X in A, Y in D) and in the A layout from mma16(Y in D, X in A).  D_b is
+// kept in both layouts (fp32; rounded to the input type only as an operand).
+//
+// Masks: with dl = n16 - 4 grp, the A-layout element i of a lane is the
+// diagonal where dl = i and lies in F_1 where i is even and dl = i + 1 (the
+// D-layout element in F_1 where i is odd and dl = i - 1).  F_2 holds elements
+// 0 and 1 of the lanes with n16 / 4 = grp and bit 1 of n16 set; F_4 all four of
+// the lanes with n16 / 8 = grp / 2, bit 2 of n16 set and grp even; F_8 all four
+// of the lanes with bit 3 of n16 set and grp < 2.
+template <typename T, int DK, int BV>
+__device__ __forceinline__ void diag_inverse(Smem<T, DK, BV> &sm, int I, const float *Na,
+                                             const float *Nd)
+{
+    typedef Path<T> PT;
+    typedef typename PT::quad Q4;
+    typedef typename Vec<T>::four V4;
+    const int lp = __lane_id(), n16 = lp & 15, grp = lp >> 4;
+    const int dl = n16 - 4 * grp;
+    f32x4 Da, Dd;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float one = dl == i ? 1.f : 0.f;
+        Da[i] = one - ((i & 1) == 0 && dl == i + 1 ? Na[i] : 0.f);
+        Dd[i] = one - ((i & 1) == 1 && dl == i - 1 ? Nd[i] : 0.f);
+    }
+    const bool f2 = (n16 >> 2) == grp && (n16 & 2);
+    const bool f4 = (n16 >> 3) == (grp >> 1) && (n16 & 4) && !(grp & 1);
+    const bool f8 = (n16 & 8) && grp < 2;
+#pragma unroll
+    for (int bs = 2; bs < 16; bs *= 2) {
+        const bool f = bs == 2 ? f2 : (bs == 4 ? f4 : f8);
+        float Fa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Fa[i] = (f && (bs > 2 || i < 2)) ? Na[i] : 0.f;
+        const Q4 da = PT::to_quad(Da);
+        const Q4 yd = PT::to_quad(PT::mma16q(PT::to_quad(Fa), PT::to_quad(Dd), zero4()));  // F D
+        Da -= PT::mma16q(yd, da, zero4());                                                   // D F D
+        if (bs < 8) Dd -= PT::mma16q(da, yd, zero4());
+    }
+    // the lane ends with T[n16][4 grp + i], T = (I + A_II)^-1
+    *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(Da);
+}
+
 // FUSED: q and k arrive unnormalised and g is replaced by decay logits z with
 // the per-head gate parameters A_log [H] and b_alpha [H][DK].  OUT = false:
 // only the final state is computed (no o, q not read, and neither P nor
@@ -844,43 +898,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
                 pv[i] = jl <= n16 ? accPt[i] : 0.f;
             }
             if (OUT) *reinterpret_cast<V4 *>(&sm.P[16 * I + n16][16 * I + 4 * grp]) = pack4<T>(pv);
-            // (I + N)^-1 by recursive block inversion.  Let D_b be the
-            // block-diagonal matrix of the inverses of the b x b diagonal blocks
-            // of I + N, and F_b the part of N that lies in the lower-left b x b
-            // block of each 2b x 2b diagonal block.  Then D_2b = D_b - D_b F_b D_b;
-            // D_1 = I gives D_2 = I - F_1, and three more levels reach D_16.
-            // Every intermediate is a block of the true inverse, whose entries
-            // stay small when the keys of a sub-block are alike (the
-            // power-series product (I - N)(I + N^2)(I + N^4)(I + N^8) instead
-            // forms powers that grow like binomial coefficients and cancel).
-            // Layouts: a lane's values of X in the A layout (X[n16][4 grp + i])
-            // are those of X^T in the D layout (X[4 grp + i][n16]), so a product
-            // X Y comes in the D layout from mma16(X in A, Y in D) and in the A
-            // layout from mma16(Y in D, X in A).  D_b is kept in both layouts
-            // (fp32; rounded to the input type only as an operand).
-            typedef typename PT::quad Q4;
-            // F_b holds N[r][c] where r, c share a 2b block, r in its lower half
-            // and c in its upper half
-            auto in_f = [](int r, int c, int bs) { return (r ^ c) < 2 * bs && (r & bs) && !(c & bs); };
-            f32x4 Da, Dd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int jl = 4 * grp + i;
-                Da[i] = (jl == n16 ? 1.f : 0.f) - (in_f(n16, jl, 1) ? Na[i] : 0.f);
-                Dd[i] = (jl == n16 ? 1.f : 0.f) - (in_f(jl, n16, 1) ? Nd[i] : 0.f);
-            }
-#pragma unroll
-            for (int bs = 2; bs < 16; bs *= 2) {
-                float Fa[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Fa[i] = in_f(n16, 4 * grp + i, bs) ? Na[i] : 0.f;
-                const Q4 da = PT::to_quad(Da);
-                const Q4 yd = PT::to_quad(PT::mma16q(PT::to_quad(Fa), PT::to_quad(Dd), zero4()));  // F D
-                Da -= PT::mma16q(yd, da, zero4());                                                   // D F D
-                if (bs < 8) Dd -= PT::mma16q(da, yd, zero4());
-            }
-            // the lane ends with T[n16][4 grp + i], T = (I + A_II)^-1
-            *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(Da);
+            diag_inverse(sm, I, Na, Nd);
         } else if (wv < 9 || wv == 10) {
             // off-diagonal block pairs.  Wave w runs on SIMD w mod 4: the three
             // pairs whose column needs a decay factor go to SIMDs 1, 2, 3, one
