@@ -464,7 +464,23 @@ def main():
                                                     "traffic": _traffic("kda_decode.hip", wd.name),
                                                     "kernel": "kda::decode_kernel",
                                                     "bytes_per_launch": dbytes}}
-        del xd
+        # the step with the output epilogue (RMSNorm, sigmoid gate) in the
+        # kernel, against the step followed by the separate epilogue kernel
+        gen = torch.Generator(device=dev).manual_seed(9)
+        gate = torch.randn(xd["v"].shape, generator=gen, device=dev).to(xd["v"].dtype)
+        rw = torch.ones(wd.dv, device=dev)
+        yd = torch.empty_like(od)
+        gms, _ = time_launches(lambda: kda.step_decode_gated(xd["q"], xd["k"], xd["v"], xd["g"],
+                                                             xd["beta"], xd["state"], gate, rw,
+                                                             out=yd),
+                               args.steps, args.warmup, torch)
+        ums, _ = time_launches(lambda: (dstep(), kda.output_gate(od, gate, rw, out=yd)),
+                               args.steps, args.warmup, torch)
+        gbytes = dbytes + wd.decode_requests * wd.H * wd.dv * ed + 4 * wd.dv
+        out["decode"]["gated"] = {"ms_per_step": gms, "GB/s": gbytes / (gms * 1e-3) / 1e9,
+                                  "unfused_ms_per_step": ums, "bytes_per_launch": gbytes,
+                                  "kernel": "kda::decode_kernel<..., gated>"}
+        del xd, gate, yd
 
     del ws
     if not args.no_two_pass:

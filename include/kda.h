@@ -225,6 +225,27 @@ kda_status kda_step_decode(const void *q, const void *k, const void *v, const fl
                            int32_t d_k, int32_t d_v, kda_dtype dtype, hipStream_t stream);
 
 /*
+ * kda_step_decode with the layer's output epilogue fused in: the step as in
+ * kda_step_decode, then, per (request, head), over the d_v columns of o
+ *     out = o / sqrt(mean(o^2) + eps) * weight * sigma(gate)
+ * (page "Notations mathematiques": row o~_t "raw output, before the gate" and
+ * the function table's RMSNorm; "Kimi K3" model tables: epsilon 1e-5 and the
+ * full-rank sigmoid output gate) -- the same epilogue as kda_output_gate, on
+ * the fp32 o before any rounding, with no separate pass over o.
+ *   gate    [N][H][d_v] dtype   gate logits
+ *   weight  [d_v] fp32          RMSNorm weight shared by the heads
+ *   eps     >= 0
+ *   out     [N][H][d_v] dtype   gated output; must not alias any input
+ *   o_raw   [N][H][d_v] dtype or NULL: the raw o as well, when given
+ * Every other argument, layout and error is as in kda_step_decode.
+ */
+kda_status kda_step_decode_gated(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, float *state, const void *gate,
+                                 const float *weight, float eps, void *out, void *o_raw,
+                                 int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 hipStream_t stream);
+
+/*
  * Chunkwise prefill with the layer's front end fused in: the same operation as
  * kda_chunk_fwd, on inputs taken one step earlier in the KDA layer.
  *   - q = L2Norm(q_raw), k = L2Norm(k_raw) per (token, head) over d_k (page

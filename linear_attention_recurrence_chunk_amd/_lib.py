@@ -62,6 +62,9 @@ def library() -> ctypes.CDLL:
     lib.kda_chunk_fwd_static_scratch_bytes.restype = sz
     lib.kda_step_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.kda_step_decode.restype = i32
+    lib.kda_step_decode_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                          i32, i32, i32, i32, i32, vp]
+    lib.kda_step_decode_gated.restype = i32
     lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                         i32, i32, i32, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd_fused.restype = i32
@@ -281,6 +284,43 @@ def step_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     st = library().kda_step_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                    _ptr(out), N, H, dk, dv, _DTYPES[q.dtype], _stream(dev))
     _check("kda_step_decode", st)
+    return out
+
+
+def step_decode_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, state: torch.Tensor, gate: torch.Tensor,
+                      weight: torch.Tensor, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                      o_raw: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step with the output epilogue fused in (kda_step_decode_gated):
+    returns RMSNorm(o) * sigmoid(gate); ``state`` is updated in place and the raw
+    o is written to ``o_raw`` when given.  Shapes as step_decode; gate like v;
+    weight [d_v] fp32."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be bf16 or fp32, got {q.dtype}")
+    dev = q.device
+    _gpu(dev)
+    _need(q, "q", ndim=(3,))
+    for name, x in (("k", k), ("v", v), ("gate", gate)):
+        _need(x, name, dtype=q.dtype, ndim=(3,), device=dev)
+    _need(g, "g", dtype=torch.float32, ndim=(3,), device=dev)
+    _need(beta, "beta", dtype=torch.float32, ndim=(2,), device=dev)
+    _need(state, "state", dtype=torch.float32, ndim=(4,), device=dev)
+    _need(weight, "weight", dtype=torch.float32, ndim=(1,), device=dev)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or tuple(v.shape[:2]) != (N, H) or \
+            gate.shape != v.shape or tuple(weight.shape) != (dv,):
+        raise ValueError("q, k, g must share a shape; v and gate [N, H, d_v]; weight [d_v]")
+    if tuple(beta.shape) != (N, H) or tuple(state.shape) != (N, H, dk, dv):
+        raise ValueError("beta must be [N, H] and state [N, H, d_k, d_v]")
+    out = _out(out, v.shape, v.dtype, dev)
+    if o_raw is not None:
+        _out(o_raw, v.shape, v.dtype, dev, "o_raw")
+    st = library().kda_step_decode_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(state), _ptr(gate), _ptr(weight), float(eps),
+                                         _ptr(out), _ptr(o_raw), N, H, dk, dv, _DTYPES[q.dtype],
+                                         _stream(dev))
+    _check("kda_step_decode_gated", st)
     return out
 
 

@@ -25,7 +25,8 @@ hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void
                                 bool is_bf16, void *o, float *sf, hipStream_t stream);
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, void *o, int64_t NH, int d,
-                         bool is_bf16, hipStream_t stream);
+                         bool is_bf16, const void *gate, const float *gw, float eps, void *out,
+                         hipStream_t stream);
 hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *w, float eps,
                               void *out, int64_t rows, int dv, bool is_bf16, bool in_f32,
                               bool out_f32, hipStream_t stream);
@@ -317,7 +318,29 @@ kda_status kda_step_decode(const void *q, const void *k, const void *v, const fl
         misaligned(state) || misaligned(o))
         return KDA_ERR_ALIGN;
     const hipError_t e = kda::launch_decode(q, k, v, g, beta, state, o, (int64_t)N * H, d_k,
-                                            dtype == KDA_BF16, stream);
+                                            dtype == KDA_BF16, nullptr, nullptr, 0.f, nullptr,
+                                            stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_step_decode_gated(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, float *state, const void *gate,
+                                 const float *weight, float eps, void *out, void *o_raw,
+                                 int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype dtype,
+                                 hipStream_t stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H < 1 || d_k < 1 || d_v < 1 || !(eps >= 0.f)) return KDA_ERR_SHAPE;
+    if (d_k != d_v || !head_size_ok(d_k)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !gate || !weight || !out) return KDA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(beta) ||
+        misaligned(state) || misaligned(gate) || misaligned(weight) || misaligned(out) ||
+        misaligned(o_raw))
+        return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_decode(q, k, v, g, beta, state, o_raw, (int64_t)N * H, d_k,
+                                            dtype == KDA_BF16, gate, weight, eps, out, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

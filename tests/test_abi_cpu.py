@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                             "kda_output_gate", "kda_short_conv", "kda_state_compose",
                             "kda_chunk_fwd_ex", "kda_output_gate_ex", "kda_chunk_fwd_algo",
                             "kda_chunk_fwd_algo_workspace_size", "kda_chunk_fwd_two_pass_static",
-                            "kda_chunk_fwd_static_scratch_bytes"])
+                            "kda_chunk_fwd_static_scratch_bytes", "kda_step_decode_gated"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -198,6 +198,27 @@ def test_chunk_fwd_static_rejects():
     assert _fwd_static(odt=7) == EUNSUP
     assert _fwd_static(total=8192, H=96, dk=128, dv=128) == ETOOLARGE   # 8K x 96 heads
     assert _fwd_static(num_seqs=0, total=0) == OK
+
+
+@gpu_visible
+def test_step_decode_gated_rejects():
+    lib = _lib.library()
+    p = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=A, k=A, v=A, g=A, beta=A, state=A, gate=A, w=A, eps=1e-5, out=A, o=None, N=4, H=2,
+                 dk=64, dv=64, dt=1)
+        a.update(kw)
+        q = lambda x: None if x is None else p(x)
+        return lib.kda_step_decode_gated(q(a["q"]), q(a["k"]), q(a["v"]), q(a["g"]), q(a["beta"]),
+                                         q(a["state"]), q(a["gate"]), q(a["w"]), a["eps"],
+                                         q(a["out"]), q(a["o"]), a["N"], a["H"], a["dk"], a["dv"],
+                                         a["dt"], None)
+    assert call(gate=None) == ENULL and call(w=None) == ENULL and call(out=None) == ENULL
+    assert call(eps=-1.0) == ESHAPE and call(N=-1) == ESHAPE
+    assert call(dk=48, dv=48) == EUNSUP and call(dt=5) == EUNSUP
+    assert call(gate=MIS) == EALIGN and call(o=MIS) == EALIGN
+    assert call(N=0) == OK
 
 
 @gpu_visible

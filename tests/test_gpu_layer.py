@@ -240,3 +240,37 @@ def test_output_gate_binding_checks_types():
         kda.output_gate(o_raw, gate, w, out=o_raw, out_dtype=torch.bfloat16)  # out must be bf16
     with pytest.raises(ValueError):
         kda.output_gate(o_raw.to(torch.float16), gate, w)               # o~ neither bf16 nor fp32
+
+
+# ---------------------------------------------------------------------------
+# decode step with the output epilogue fused in (kda_step_decode_gated)
+@pytest.mark.parametrize("dtype,d,N,H", [(torch.bfloat16, 128, 7, 3), (torch.bfloat16, 64, 7, 3),
+                                         (torch.bfloat16, 32, 7, 3), (torch.float32, 128, 7, 3),
+                                         (torch.float32, 64, 5, 2), (torch.bfloat16, 128, 256, 96)])
+def test_decode_gated_against_oracle(dtype, d, N, H):
+    from linear_attention_recurrence_chunk_amd import inputs
+    w = inputs.custom(H=H, dk=d, dv=d, dtype=dtype, decode_requests=N, state_std=0.5)
+    x = inputs.decode_inputs(w, seed=200 + d, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(201 + d)
+    gate = torch.randn(x["v"].shape, generator=gen, device=dev).to(dtype)
+    wt = 1.0 + 0.1 * torch.randn(d, generator=gen, device=dev)
+    st0 = x["state"].clone()
+    st_plain = x["state"].clone()
+    o_raw = torch.empty_like(x["v"])
+    y = kda.step_decode_gated(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], gate, wt,
+                              1e-5, o_raw=o_raw)
+    o_plain = kda.step_decode(x["q"], x["k"], x["v"], x["g"], x["beta"], st_plain)
+    torch.cuda.synchronize()
+    # the step is the plain kernel's, bit for bit
+    assert torch.equal(o_raw, o_plain) and torch.equal(x["state"], st_plain)
+    o_ref, s_ref = oracle.decode(x["q"], x["k"], x["v"], x["g"], x["beta"], st0)
+    y_ref = L.output_gate(o_ref, _np(gate), _np(wt), eps=1e-5)
+    tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    e, es = _rel(_np(y), y_ref), _rel(_np(x["state"]), s_ref)
+    print(f"[layer] decode gated {dtype} d={d} N={N} H={H}: out {e:.3e} state {es:.3e}", flush=True)
+    assert e <= tol and es <= tol
+    # without o_raw the gated output is the same
+    st1 = st0.clone()
+    y2 = kda.step_decode_gated(x["q"], x["k"], x["v"], x["g"], x["beta"], st1, gate, wt, 1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y) and torch.equal(st1, st_plain)
