@@ -225,30 +225,51 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                                       "kernel": "kda::short_conv_kernel (+ state update)",
                                       "bytes_per_launch": cb}}
     del li, o, og, xc, st
-    # segment summaries of the prefill sequence split in 4, and their scan
+    # context-parallel segments: the sequence split in P = 4 ("Glossaire",
+    # entry "KCP").  Each of P devices would compute its segment's summaries,
+    # take part in the scan and run its segment's prefill from the state the
+    # scan hands it; on one device that critical path is timed piece by piece.
     cu = x["cu_seqlens"]
     if n_seq == 1:
-        T = n_tok
+        T, P = n_tok, 4
         cuts = torch.tensor([0, T // 4, T // 2, 3 * T // 4, T], dtype=torch.int32, device=dev)
         M, St = kda.kcp_summaries(x["q"], x["k"], x["v"], x["g"], x["beta"], cuts)
         ms_sum, _ = time_launches(lambda: kda.kcp_summaries(x["q"], x["k"], x["v"], x["g"],
-                                                            x["beta"], cuts), 3, 1, torch)
-        ms_scan, _ = time_launches(lambda: kda.kcp_scan(M, St), args.steps, args.warmup, torch)
+                                                            x["beta"], cuts), 5, 2, torch)
+        seg = slice(0, T // 4)
+        xs = {n: x[n][seg] for n in ("q", "k", "v", "g", "beta")}
+        cu1 = torch.tensor([0, T // 4], dtype=torch.int32, device=dev)
+        ms_seg_sum, _ = time_launches(lambda: kda.kcp_summaries(xs["q"], xs["k"], xs["v"], xs["g"],
+                                                                xs["beta"], cu1), 5, 2, torch)
+        S_in, S_fin = kda.kcp_scan(M, St)
+        ms_scan, _ = time_launches(lambda: kda.kcp_scan(M, St, S_in=S_in, S_final=S_fin),
+                                   args.steps, args.warmup, torch)
+        s_in1 = S_in[1].unsqueeze(0).contiguous()
+        os_ = torch.empty_like(xs["v"])
+        sfs = torch.empty_like(s_in1)
+        ms_seg, _ = time_launches(lambda: kda.chunk_fwd(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"],
+                                                        s_in1, cu1, chunk_size=w.chunk, out=os_,
+                                                        final_state=sfs),
+                                  args.steps, args.warmup, torch)
+        d = w.dk
+        sb = P * w.H * d * d * 4 * 3 + w.H * d * d * 4
+        res["kcp"] = {"segments": P, "summaries_all_segments_ms": ms_sum,
+                      "segment_summaries_ms": ms_seg_sum, "scan_ms": ms_scan,
+                      "segment_prefill_ms": ms_seg,
+                      "critical_path_ms": ms_seg_sum + ms_scan + ms_seg,
+                      "scan": {"roofline": {"bound": "hbm", "achieved": _gbs(sb, ms_scan),
+                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": _gbs(sb, ms_scan) / HBM_PEAK_GBS,
+                                            "traffic": None, "kernel": "kda::scan_kernel",
+                                            "bytes_per_launch": sb}}}
         cnt = w.H
         out = torch.empty_like(St[0])
         ms_c, _ = time_launches(lambda: kda.state_compose(M[0], St[0], St[1], out=out),
                                 args.steps, args.warmup, torch)
-        d = w.dk
-        res["kcp"] = {"segments": 4, "summaries_ms": ms_sum, "scan_ms": ms_scan,
-                      "compose": {"count": cnt, "ms": ms_c,
-                                  "TFLOP/s": 2 * d ** 3 * cnt / (ms_c * 1e-3) / 1e12,
-                                  "GB/s": _gbs(4 * d * d * 4 * cnt, ms_c),
-                                  "roofline": {"bound": "hbm", "achieved": _gbs(4 * d * d * 4 * cnt, ms_c),
-                                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                               "frac": _gbs(4 * d * d * 4 * cnt, ms_c) / HBM_PEAK_GBS,
-                                               "traffic": None, "kernel": "kda::compose_kernel",
-                                               "bytes_per_launch": 4 * d * d * 4 * cnt}}}
-        del M, St, out
+        res["kcp"]["compose"] = {"count": cnt, "ms": ms_c,
+                                 "TFLOP/s": 2 * d ** 3 * cnt / (ms_c * 1e-3) / 1e12,
+                                 "GB/s": _gbs(4 * d * d * 4 * cnt, ms_c)}
+        del M, St, out, S_in, S_fin, xs, os_, sfs
     # nano-K3 shapes
     wn = inputs.WORKLOADS["nano_k3_prefill"]
     xn = inputs.prefill_inputs(wn, seed=2, device=dev)
@@ -487,6 +508,8 @@ def main():
         out["two_pass"] = bench_two_pass(args, w, x, torch, kda, dev)
     if not args.no_layer:
         out["layer"] = bench_layer(args, w, x, torch, kda, inputs, dev)
+        if "kcp" in out["layer"]:
+            out["layer"]["kcp"]["whole_prefill_ms"] = ms
     if not args.no_configs:
         out["other_configs"] = bench_configs(args, torch, kda, inputs, dev)
 

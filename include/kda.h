@@ -347,6 +347,45 @@ kda_status kda_state_compose(const float *M, const float *S_in, const float *S_t
                              float *S_out, int64_t count, int32_t d_k, int32_t d_v,
                              hipStream_t stream);
 
+/*
+ * Both summaries of each of num_segments packed segments, for all heads, in
+ * one launch ("Glossaire", entry "KCP"; notation table rows M_t and S~):
+ *     M[s]       = the product of segment s's transitions, M_T ... M_1 with
+ *                  M_t = (I - beta_t k_t k_t^T) Diag(alpha_t): the final state
+ *                  of the segment run from S = I with zero values;
+ *     S_tilde[s] = the segment's final state from S = 0 with its values.
+ * A workgroup runs one 64-column slice of one of the two: the slices of M and
+ * of S~ of a head read the same k, g, beta, which the two runs share through
+ * the cache instead of two launches reading them.
+ *   k, v, g, beta, cu_seqlens   as in kda_chunk_fwd, the segments as sequences
+ *   M, S_tilde  [num_segments][H][d][d] fp32 out
+ * d in {32, 64, 128} for bf16, {32, 64} for fp32 (else KDA_ERR_UNSUPPORTED;
+ * two state-only kda_chunk_fwd calls give the summaries there); chunk_size
+ * 64.  Other errors as kda_chunk_fwd.  One launch on `stream`.
+ */
+kda_status kda_kcp_summaries(const void *k, const void *v, const float *g, const float *beta,
+                             const int32_t *cu_seqlens, int32_t num_segments,
+                             int64_t total_tokens, int32_t H, int32_t d, int32_t chunk_size,
+                             kda_dtype dtype, float *M, float *S_tilde, hipStream_t stream);
+
+/*
+ * The whole scan over the summaries of P consecutive segments of each head,
+ * in one launch ("Glossaire", entry "KCP": the summaries compose
+ * associatively; notation table rows M_t and S~):
+ *     S_in[0] = S0,  S_in[r + 1] = M[r] S_in[r] + S_tilde[r],  S_final = S_in[P]
+ * in fp32.  (M[r], S_tilde[r]) are segment r's summaries as described for
+ * kda_state_compose, for all heads at once.
+ *   M, S_tilde  [P][H][d][d] fp32 (may be NULL when P == 0)
+ *   S0          [H][d][d] fp32, or NULL for a zero initial state
+ *   S_in        [P][H][d][d] fp32 out, the state entering each segment, or
+ *               NULL when not wanted
+ *   S_final     [H][d][d] fp32 out; may alias S0, must not alias the others
+ * d in {32, 64, 128} (d_k == d_v).  One workgroup per (head, 32 columns) runs
+ * the P steps in order; one launch on `stream`.
+ */
+kda_status kda_segment_scan(const float *M, const float *S_tilde, const float *S0, float *S_in,
+                            float *S_final, int32_t P, int32_t H, int32_t d, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *kda_status_string(kda_status status);
 

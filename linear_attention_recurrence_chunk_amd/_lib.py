@@ -65,6 +65,10 @@ def library() -> ctypes.CDLL:
     lib.kda_step_decode_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                           i32, i32, i32, i32, i32, vp]
     lib.kda_step_decode_gated.restype = i32
+    lib.kda_segment_scan.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.kda_segment_scan.restype = i32
+    lib.kda_kcp_summaries.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp]
+    lib.kda_kcp_summaries.restype = i32
     lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                         i32, i32, i32, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd_fused.restype = i32
@@ -470,31 +474,62 @@ def state_compose(M: torch.Tensor, S_in: torch.Tensor, S_tilde: torch.Tensor,
     return out
 
 
-def kcp_summaries(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+def kcp_summaries(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, cu_seqlens: torch.Tensor
                   ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Per-segment summaries (M, S~) of packed segments, each with one
-    state-only kda_chunk_fwd launch over all segments at once: S~ from S = 0,
-    and M from S = I with zero values (d_v = d_k).  q is not needed.
+    """Per-segment summaries (M, S~) of packed segments: M from S = I with zero
+    values, S~ from S = 0 (d_v = d_k).  One kda_kcp_summaries launch where it
+    supports the shape (bf16, or fp32 up to d = 64); fp32 at d = 128 takes two
+    state-only kda_chunk_fwd calls instead.  q is not needed.
     Returns ([P, H, d, d], [P, H, d, d_v])."""
     P = cu_seqlens.shape[0] - 1
+    dev = k.device
+    _gpu(dev)
+    _need(k, "k", ndim=(3,))
     H, dk = k.shape[-2:]
-    _, S_t = chunk_fwd(None, k, v, g, beta, cu_seqlens=cu_seqlens, output=False)
-    eye = torch.eye(dk, dtype=torch.float32, device=k.device).expand(P, H, dk, dk).contiguous()
-    _, M = chunk_fwd(None, k, None, g, beta, initial_state=eye, cu_seqlens=cu_seqlens,
-                     output=False)
+    if k.dtype == torch.float32 and dk > 64:
+        _, S_t = chunk_fwd(None, k, v, g, beta, cu_seqlens=cu_seqlens, output=False)
+        eye = torch.eye(dk, dtype=torch.float32, device=dev).expand(P, H, dk, dk).contiguous()
+        _, M = chunk_fwd(None, k, None, g, beta, initial_state=eye, cu_seqlens=cu_seqlens,
+                         output=False)
+        return M, S_t
+    if k.dtype not in _DTYPES:
+        raise ValueError(f"k must be bf16 or fp32, got {k.dtype}")
+    _need(v, "v", dtype=k.dtype, ndim=(3,), device=dev)
+    _need(g, "g", dtype=torch.float32, ndim=(3,), device=dev)
+    _need(beta, "beta", dtype=torch.float32, ndim=(2,), device=dev)
+    _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, ndim=(1,), device=dev)
+    n = k.shape[0]
+    if v.shape != k.shape or g.shape != k.shape or tuple(beta.shape) != (n, H):
+        raise ValueError("k, v, g must be [N_tok, H, d] and beta [N_tok, H]")
+    M = torch.empty((P, H, dk, dk), dtype=torch.float32, device=dev)
+    S_t = torch.empty_like(M)
+    st = library().kda_kcp_summaries(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), P, n,
+                                     H, dk, 64, _DTYPES[k.dtype], _ptr(M), _ptr(S_t), _stream(dev))
+    _check("kda_kcp_summaries", st)
     return M, S_t
 
 
-def kcp_scan(M: torch.Tensor, S_tilde: torch.Tensor,
-             S0: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """States entering each segment and the final state: S_in[0] = S0 (or 0),
-    S_in[r + 1] = M[r] S_in[r] + S~[r], one kda_state_compose launch per
-    segment (over all heads)."""
-    P = M.shape[0]
-    S = torch.zeros_like(S_tilde[0]) if S0 is None else S0.contiguous()
-    S_in = torch.empty_like(S_tilde)
-    for r in range(P):
-        S_in[r].copy_(S)
-        S = state_compose(M[r], S, S_tilde[r])
-    return S_in, S
+def kcp_scan(M: torch.Tensor, S_tilde: torch.Tensor, S0: Optional[torch.Tensor] = None,
+             S_in: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """States entering each segment and the final state, one kda_segment_scan
+    launch: S_in[0] = S0 (or 0), S_in[r + 1] = M[r] S_in[r] + S~[r].
+    M, S_tilde [P, H, d, d] fp32; S0 [H, d, d] fp32 or None."""
+    _need(M, "M", dtype=torch.float32, ndim=(4,))
+    dev = M.device
+    _gpu(dev)
+    _need(S_tilde, "S_tilde", dtype=torch.float32, ndim=(4,), device=dev)
+    P, H, d = M.shape[:3]
+    if tuple(M.shape) != (P, H, d, d) or S_tilde.shape != M.shape:
+        raise ValueError("M and S_tilde must both be [P, H, d, d]")
+    if S0 is not None:
+        _need(S0, "S0", dtype=torch.float32, ndim=(3,), device=dev)
+        if tuple(S0.shape) != (H, d, d):
+            raise ValueError(f"S0 must be [{H}, {d}, {d}]")
+    S_in = _out(S_in, M.shape, torch.float32, dev, "S_in")
+    S_final = _out(S_final, (H, d, d), torch.float32, dev, "S_final")
+    st = library().kda_segment_scan(_ptr(M), _ptr(S_tilde), _ptr(S0), _ptr(S_in), _ptr(S_final),
+                                    P, H, d, _stream(dev))
+    _check("kda_segment_scan", st)
+    return S_in, S_final

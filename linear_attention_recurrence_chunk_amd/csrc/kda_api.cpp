@@ -35,6 +35,11 @@ hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, i
                              hipStream_t stream);
 hipError_t launch_compose(const float *M, const float *S_in, const float *S_tilde, float *S_out,
                           int64_t count, int d, hipStream_t stream);
+hipError_t launch_scan(const float *M, const float *St, const float *S0, float *S_in,
+                       float *S_fin, int P, int H, int d, hipStream_t stream);
+hipError_t launch_kcp_summaries(const void *k, const void *v, const float *g, const float *beta,
+                                const int32_t *cu, int num_seqs, int64_t seq_len, int H, int d,
+                                bool is_bf16, float *M, float *St, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -301,6 +306,41 @@ kda_status kda_state_compose(const float *M, const float *S_in, const float *S_t
     if (misaligned(M) || misaligned(S_in) || misaligned(S_tilde) || misaligned(S_out))
         return KDA_ERR_ALIGN;
     const hipError_t e = kda::launch_compose(M, S_in, S_tilde, S_out, count, d_k, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_kcp_summaries(const void *k, const void *v, const float *g, const float *beta,
+                             const int32_t *cu_seqlens, int32_t num_segments,
+                             int64_t total_tokens, int32_t H, int32_t d, int32_t chunk_size,
+                             kda_dtype dtype, float *M, float *S_tilde, hipStream_t stream)
+{
+    // the same inputs as a state-only prefill of the segments (q unused)
+    const kda_status st =
+        prefill_check(nullptr, k, v, g, beta, nullptr, cu_seqlens, num_segments, total_tokens, H,
+                      d, d, chunk_size, dtype, KDA_ALGO_FUSED, nullptr, S_tilde, nullptr, 0, true);
+    if (st != KDA_OK) return st;
+    if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)num_segments * H * 16 > INT32_MAX) return KDA_ERR_SHAPE;
+    if (num_segments == 0) return KDA_OK;
+    if (!M || !S_tilde || (total_tokens > 0 && !v)) return KDA_ERR_NULL;
+    if (misaligned(M)) return KDA_ERR_ALIGN;
+    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_segments;
+    const hipError_t e = kda::launch_kcp_summaries(k, v, g, beta, cu_seqlens, num_segments, seq_len,
+                                                   H, d, dtype == KDA_BF16, M, S_tilde, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_segment_scan(const float *M, const float *S_tilde, const float *S0, float *S_in,
+                            float *S_final, int32_t P, int32_t H, int32_t d, hipStream_t stream)
+{
+    if (P < 0 || H < 1 || d < 1) return KDA_ERR_SHAPE;
+    if (d != 32 && d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)H * (d / 32) > INT32_MAX) return KDA_ERR_SHAPE;
+    if (!S_final || (P > 0 && (!M || !S_tilde))) return KDA_ERR_NULL;
+    if (misaligned(M) || misaligned(S_tilde) || misaligned(S0) || misaligned(S_in) ||
+        misaligned(S_final))
+        return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_scan(M, S_tilde, S0, S_in, S_final, P, H, d, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

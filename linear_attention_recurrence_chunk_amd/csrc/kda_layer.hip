@@ -7,7 +7,8 @@
 //     (function table "ShortConv", "Glossaire" entry "ShortConv", model table
 //     "ShortConv kernel (KDA) 4");
 //   - state composition for context-parallel segments: S_out = M S_in + S~
-//     ("Glossaire", entry "KCP"; notation table rows M_t and S~).
+//     ("Glossaire", entry "KCP"; notation table rows M_t and S~), one step
+//     over a batch, or the whole scan over P segments in one launch.
 // The first two are elementwise and bound by HBM bandwidth: coalesced accesses
 // (16-byte lanes for the gate, 8-byte for ShortConv), fp32 arithmetic.  The
 // composition is a batch of dense fp32 products on the matrix cores
@@ -368,6 +369,114 @@ hipError_t launch_compose(const float *M, const float *S_in, const float *S_tild
         case 32: return launch_compose_t<32>(M, S_in, S_tilde, S_out, count, stream);
         case 64: return launch_compose_t<64>(M, S_in, S_tilde, S_out, count, stream);
         case 128: return launch_compose_t<128>(M, S_in, S_tilde, S_out, count, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Scan over P segment summaries in one launch: for each head,
+//     S_in[0] = S0,  S_in[r + 1] = M[r] S_in[r] + S~[r],  S_final = S_in[P].
+// The columns of S evolve independently, so one workgroup owns one head's
+// 32-column block for the whole scan and keeps it in LDS (d x 32 fp32, rows
+// padded to 36 floats so that the four K rows of a fragment read fall in
+// different banks).  Each step, wave w computes TPW 16 x 16 tiles of
+// M[r] S + S~[r] on v_mfma_f32_16x16x4_f32; within a 16-wide K block, lane
+// group grp supplies K index kb + 4 grp + s at sub-step s to both operands, so
+// that its four M values are one 16-byte read.  M[r] and S~[r] are read once
+// per column block (from L2 after the first), S_in[r] is written once.
+template <int D>
+__global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ M,
+                                                   const float *__restrict__ St,
+                                                   const float *S0, float *__restrict__ S_in,
+                                                   float *S_fin, int P, int H)
+{
+    constexpr int CB = 32, NCB = D / CB, NCT = CB / 16, LDW = CB + 4;
+    constexpr int TILES = (D / 16) * NCT, TPW = TILES / 4;
+    static_assert(TPW >= 1 && TILES % 4 == 0, "shape");
+    __shared__ float sS[D][LDW];
+
+    const int lane = threadIdx.x & 63, n16 = lane & 15, grp = lane >> 4;
+    const int w = threadIdx.x >> 6;
+    const int h = blockIdx.x / NCB, c0 = (blockIdx.x % NCB) * CB;
+    const int64_t DD = (int64_t)D * D;
+    // block copies: thread t moves 4 consecutive columns of rows t / 8 + 32 j
+    const int cr = threadIdx.x >> 3, cc = (threadIdx.x & 7) * 4;
+
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+        f32x4 x = zero4();
+        if (S0)
+            x = *reinterpret_cast<const f32x4 *>(S0 + h * DD + (int64_t)(cr + 32 * j) * D + c0 + cc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sS[cr + 32 * j][cc + i] = x[i];
+    }
+
+    for (int r = 0; r < P; ++r) {
+        __syncthreads();   // S complete in LDS
+        const int64_t base = ((int64_t)r * H + h) * DD;
+        if (S_in) {
+#pragma unroll
+            for (int j = 0; j < D / 32; ++j) {
+                const int row = cr + 32 * j;
+                *reinterpret_cast<f32x4 *>(S_in + base + (int64_t)row * D + c0 + cc) =
+                    f32x4{sS[row][cc], sS[row][cc + 1], sS[row][cc + 2], sS[row][cc + 3]};
+            }
+        }
+        f32x4 acc[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int tile = w * TPW + t, rs = tile / NCT, ct = tile % NCT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[t][i] = St[base + (int64_t)(16 * rs + 4 * grp + i) * D + c0 + 16 * ct + n16];
+        }
+        const float *Mr = M + base;
+#pragma unroll 2
+        for (int kb = 0; kb < D; kb += 16) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int tile = w * TPW + t, rs = tile / NCT, ct = tile % NCT;
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(
+                    Mr + (int64_t)(16 * rs + n16) * D + kb + 4 * grp);
+#pragma unroll
+                for (int sub = 0; sub < 4; ++sub)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        a[sub], sS[kb + 4 * grp + sub][16 * ct + n16], acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();   // every read of S done
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int tile = w * TPW + t, rs = tile / NCT, ct = tile % NCT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sS[16 * rs + 4 * grp + i][16 * ct + n16] = acc[t][i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+        const int row = cr + 32 * j;
+        *reinterpret_cast<f32x4 *>(S_fin + h * DD + (int64_t)row * D + c0 + cc) =
+            f32x4{sS[row][cc], sS[row][cc + 1], sS[row][cc + 2], sS[row][cc + 3]};
+    }
+}
+
+template <int D>
+static hipError_t launch_scan_t(const float *M, const float *St, const float *S0, float *S_in,
+                                float *S_fin, int P, int H, hipStream_t stream)
+{
+    hipLaunchKernelGGL((scan_kernel<D>), dim3((unsigned)(H * (D / 32))), dim3(256), 0, stream, M,
+                       St, S0, S_in, S_fin, P, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const float *M, const float *St, const float *S0, float *S_in,
+                       float *S_fin, int P, int H, int d, hipStream_t stream)
+{
+    switch (d) {
+        case 32: return launch_scan_t<32>(M, St, S0, S_in, S_fin, P, H, stream);
+        case 64: return launch_scan_t<64>(M, St, S0, S_in, S_fin, P, H, stream);
+        case 128: return launch_scan_t<128>(M, St, S0, S_in, S_fin, P, H, stream);
     }
     return hipErrorInvalidValue;
 }

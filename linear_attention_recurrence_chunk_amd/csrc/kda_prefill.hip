@@ -732,20 +732,27 @@ __device__ __forceinline__ void diag_inverse(Smem<T, DK, BV> &sm, int I, const f
 // only the final state is computed (no o, q not read, and neither P nor
 // (Q o e^G) S is formed); v == nullptr stands for zero values.  TO: the type
 // of o (the input type, or fp32 for bf16 inputs).
-template <typename T, int DK, int BV, int DV, bool FUSED, bool OUT, typename TO>
+// KCP (with OUT = false): a segment's two summaries in one launch ("Glossaire",
+// entry "KCP"; notation table rows M_t and S~).  The value slices are doubled:
+// those of the first half run the transition product, from S = I with zero
+// values, and write M to mfinal; those of the second half run from S = 0 with
+// the values and write S~ to sfinal.  s0 is not read.
+template <typename T, int DK, int BV, int DV, bool FUSED, bool OUT, typename TO, bool KCP = false>
 __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ s0, const int32_t *__restrict__ cu_seqlens, int num_seqs,
     int64_t seq_len, int H, TO *__restrict__ o, float *__restrict__ sfinal,
-    const T *__restrict__ z, const float *__restrict__ A_log, const float *__restrict__ b_alpha)
+    const T *__restrict__ z, const float *__restrict__ A_log, const float *__restrict__ b_alpha,
+    float *__restrict__ mfinal)
 {
     typedef Cfg<T, DK, BV> Cf;
     typedef Path<T> PT;
     typedef Smem<T, DK, BV> Sm;
     typedef typename Vec<T>::four V4;
     constexpr int C = Cf::C, NB = Cf::NB, NT = Cf::NT, KS = PT::KS, KPL = PT::KPL;
-    constexpr int NSLICE = DV / BV;
+    static_assert(!KCP || (!OUT && !FUSED), "summaries are state-only");
+    constexpr int NSLICE = (KCP ? 2 : 1) * DV / BV;
     constexpr int NVT = Cf::NVT, NCT = Cf::NCT;
     __shared__ __align__(16) Sm sm;
 
@@ -764,6 +771,8 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const int seq = (int)(w / ((int64_t)H * NSLICE));
     const int head = (int)((w / NSLICE) % H);
     const int slice = (int)(w % NSLICE);
+    const bool trans = KCP && slice < DV / BV;      // a transition-product slice
+    const T *const vsrc = trans ? nullptr : v;
     SeqView sv;
     if (cu_seqlens) {
         sv.bos = cu_seqlens[seq];
@@ -774,7 +783,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     }
     sv.head = head;
     sv.H = H;
-    sv.v0 = slice * BV;
+    sv.v0 = (slice % (DV / BV)) * BV;
 
     const int t = threadIdx.x;
     const int lane = lane_id(), wv = wave_id();
@@ -793,7 +802,13 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
-            if (s0) {
+            if (KCP) {
+                if (trans) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        W[vt][i] = 16 * ct + 4 * grp + i == sv.v0 + 16 * vt + n16 ? 1.f : 0.f;
+                }
+            } else if (s0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     W[vt][i] = s0[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16];
@@ -834,7 +849,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const int64_t nchunks = (sv.eos - sv.bos + C - 1) / C;
     ChunkRegs<T, DK, BV> R;
     if (nchunks > 0) {
-        load_chunk<FUSED, OUT>(R, LOAD_ALL, sv, sv.bos, q, k, v, g, z, beta, DV);
+        load_chunk<FUSED, OUT>(R, LOAD_ALL, sv, sv.bos, q, k, vsrc, g, z, beta, DV);
         if (FUSED) {
             norm_partials(sm, R);
             __syncthreads();
@@ -853,7 +868,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         const int64_t t0 = sv.bos + ch * C;
         const int nv = rows_in(t0, sv.eos, C);           // rows of this chunk in the sequence
         const bool more = ch + 1 < nchunks;
-        if (more) load_chunk<FUSED, OUT>(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, v, g, z, beta, DV);
+        if (more) load_chunk<FUSED, OUT>(R, LOAD_G | LOAD_KQ, sv, t0 + C, q, k, vsrc, g, z, beta, DV);
 
         // ================= AP
         // (lane indices inside the loop come from __lane_id(), which the
@@ -922,7 +937,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             if (c < DK) decay_tables(sm, c, (int)(ch & 1));
         }
         __syncthreads();   // ---------------------------------------------- B1
-        if (more) load_chunk<FUSED, OUT>(R, LOAD_VB, sv, t0 + C, q, k, v, g, z, beta, DV);
+        if (more) load_chunk<FUSED, OUT>(R, LOAD_VB, sv, t0 + C, q, k, vsrc, g, z, beta, DV);
 
         // ================= YZ: state read-out and R = B (V - Y); the state
         // waves take their Kbar^T fragments before the next chunk's E
@@ -1048,13 +1063,14 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
         if (more) chunk_ref_rows<OUT>(sm, wv);
     }
 
-    if (sfinal && state_wave) {
+    float *const sf = trans ? mfinal : sfinal;
+    if (sf && state_wave) {
         const int n16 = lane & 15, grp = lane >> 4;
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sfinal[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16] = W[vt][i];
+                sf[sbase + (int64_t)(16 * ct + 4 * grp + i) * DV + 16 * vt + n16] = W[vt][i];
         }
     }
 }
@@ -1073,8 +1089,46 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
     hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FUSED, OUT, TO>), dim3((unsigned)nwork),
                        dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)q, (const T *)k,
                        (const T *)v, g, beta, s0, cu, num_seqs, seq_len, H, (TO *)o, sf,
-                       (const T *)z, A_log, b_alpha);
+                       (const T *)z, A_log, b_alpha, (float *)nullptr);
     return hipGetLastError();
+}
+
+// Segment summaries (M, S~) of packed segments in one launch.
+template <typename T, int D, int BV>
+static hipError_t launch_kcp_t(const void *k, const void *v, const float *g, const float *beta,
+                               const int32_t *cu, int num_seqs, int64_t seq_len, int H, float *M,
+                               float *St, hipStream_t stream)
+{
+    const int64_t nwork = (int64_t)num_seqs * H * (2 * D / BV);
+    if (nwork == 0) return hipSuccess;
+    if ((int64_t)H * D * 4 >= (int64_t)1 << 24) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, false, false, T, true>), dim3((unsigned)nwork),
+                       dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)nullptr, (const T *)k,
+                       (const T *)v, g, beta, (const float *)nullptr, cu, num_seqs, seq_len, H,
+                       (T *)nullptr, St, (const T *)nullptr, (const float *)nullptr,
+                       (const float *)nullptr, M);
+    return hipGetLastError();
+}
+
+hipError_t launch_kcp_summaries(const void *k, const void *v, const float *g, const float *beta,
+                                const int32_t *cu, int num_seqs, int64_t seq_len, int H, int d,
+                                bool is_bf16, float *M, float *St, hipStream_t stream)
+{
+#define KDA_KCP_ARGS k, v, g, beta, cu, num_seqs, seq_len, H, M, St, stream
+    if (is_bf16) {
+        switch (d) {
+            case 32: return launch_kcp_t<bf16, 32, 32>(KDA_KCP_ARGS);
+            case 64: return launch_kcp_t<bf16, 64, 64>(KDA_KCP_ARGS);
+            case 128: return launch_kcp_t<bf16, 128, 64>(KDA_KCP_ARGS);
+        }
+    } else {
+        switch (d) {
+            case 32: return launch_kcp_t<float, 32, 32>(KDA_KCP_ARGS);
+            case 64: return launch_kcp_t<float, 64, 32>(KDA_KCP_ARGS);
+        }
+    }
+#undef KDA_KCP_ARGS
+    return hipErrorInvalidValue;
 }
 
 // O32: o in fp32 for bf16 inputs (only the unfused kernel with an output).

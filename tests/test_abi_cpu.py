@@ -33,7 +33,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                             "kda_output_gate", "kda_short_conv", "kda_state_compose",
                             "kda_chunk_fwd_ex", "kda_output_gate_ex", "kda_chunk_fwd_algo",
                             "kda_chunk_fwd_algo_workspace_size", "kda_chunk_fwd_two_pass_static",
-                            "kda_chunk_fwd_static_scratch_bytes", "kda_step_decode_gated"])
+                            "kda_chunk_fwd_static_scratch_bytes", "kda_step_decode_gated", "kda_segment_scan",
+                            "kda_kcp_summaries"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -320,3 +321,19 @@ def test_layer_steps_reject():
     assert lib.kda_state_compose(p(A), None, p(A), p(A), 4, 64, 64, None) == ENULL
     assert lib.kda_state_compose(p(A), p(A), p(A), p(MIS), 4, 64, 64, None) == EALIGN
     assert lib.kda_state_compose(None, None, None, None, 0, 64, 64, None) == OK
+    # segment summaries in one launch
+    ks = lambda **kw: (lambda a: lib.kda_kcp_summaries(
+        a["k"], a["v"], p(A), p(A), None, a["P"], a["n"], 2, a["d"], a["C"], a["dt"], a["M"], a["S"],
+        None))({**dict(k=p(A), v=p(A), P=2, n=128, d=64, C=64, dt=1, M=p(A), S=p(A)), **kw})
+    assert ks(d=128, dt=0) == EUNSUP and ks(C=128) == EUNSUP and ks(d=48) == EUNSUP
+    assert ks(M=None) == ENULL and ks(S=None) == ENULL and ks(v=None) == ENULL
+    assert ks(k=None) == ENULL and ks(M=p(MIS)) == EALIGN and ks(n=127) == ESHAPE
+    assert ks(P=0, n=0) == OK
+    # segment scan
+    assert lib.kda_segment_scan(p(A), p(A), None, None, p(A), -1, 2, 64, None) == ESHAPE
+    assert lib.kda_segment_scan(p(A), p(A), None, None, p(A), 3, 0, 64, None) == ESHAPE
+    assert lib.kda_segment_scan(p(A), p(A), None, None, p(A), 3, 2, 48, None) == EUNSUP
+    assert lib.kda_segment_scan(p(A), p(A), None, None, None, 3, 2, 64, None) == ENULL
+    assert lib.kda_segment_scan(None, p(A), None, None, p(A), 3, 2, 64, None) == ENULL
+    assert lib.kda_segment_scan(p(A), p(A), p(MIS), None, p(A), 3, 2, 64, None) == EALIGN
+    assert lib.kda_segment_scan(p(A), p(A), None, p(MIS), p(A), 3, 2, 64, None) == EALIGN

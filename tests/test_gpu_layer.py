@@ -169,6 +169,70 @@ def test_state_compose(d):
     assert e <= 1e-5
 
 
+@pytest.mark.parametrize("d,P,H,with_s0", [(32, 5, 3, True), (64, 1, 2, False), (128, 8, 4, True),
+                                           (128, 0, 2, True), (64, 3, 5, False),
+                                           (128, 4, 96, True)])
+def test_segment_scan_against_oracle(d, P, H, with_s0):
+    gen = torch.Generator(device=dev).manual_seed(300 + d + P)
+    M = 0.9 * torch.randn(P, H, d, d, generator=gen, device=dev) / np.sqrt(d)
+    St = torch.randn(P, H, d, d, generator=gen, device=dev)
+    S0 = torch.randn(H, d, d, generator=gen, device=dev) if with_s0 else None
+    S_in, S_fin = kda.kcp_scan(M, St, S0)
+    torch.cuda.synchronize()
+    Mn, Sn = _np(M), _np(St)
+    hs = range(H) if H <= 8 else (0, 37, H - 1)
+    for h in hs:
+        s_in_ref, s_fin_ref = L.kcp_scan(Mn[:, h], Sn[:, h], None if S0 is None else _np(S0[h]))
+        e_fin = _rel(_np(S_fin[h]), s_fin_ref)
+        e_in = _rel(_np(S_in[:, h]), s_in_ref) if P else 0.0
+        assert e_fin <= 2e-5 and e_in <= 2e-5, (h, e_fin, e_in)
+    print(f"[parity] segment scan d={d} P={P} H={H}: final {e_fin:.2e}", flush=True)
+    # in place on S0, and without the entering states: the same final state
+    if S0 is not None:
+        S1 = S0.clone()
+        lib = kda.library()
+        p = lambda x: None if x is None else __import__("ctypes").c_void_p(x.data_ptr())
+        assert lib.kda_segment_scan(p(M) if P else None, p(St) if P else None, p(S1), None, p(S1),
+                                    P, H, d, None) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(S1, S_fin)
+
+
+@pytest.mark.parametrize("dtype,d,cuts", [(torch.bfloat16, 128, [0, 500, 501, 621, 2048]),
+                                          (torch.bfloat16, 64, [0, 0, 64, 300]),
+                                          (torch.bfloat16, 32, [0, 77, 333]),
+                                          (torch.float32, 64, [0, 129, 130, 400]),
+                                          (torch.float32, 32, [0, 1, 65])])
+def test_kcp_summaries_one_launch(dtype, d, cuts):
+    """The one-launch summaries equal the two state-only prefills they replace
+    (the same slices run the same arithmetic), and M matches the oracle's
+    product of transitions."""
+    H = 3
+    T = cuts[-1]
+    gen = torch.Generator(device=dev).manual_seed(40 + d)
+    r = lambda *s: torch.randn(*s, generator=gen, device=dev)
+    k = torch.nn.functional.normalize(r(T, H, d), dim=-1).to(dtype)
+    v = r(T, H, d).to(dtype)
+    g = -5.0 * torch.sigmoid(r(T, H, d) - 6.0)
+    beta = torch.sigmoid(r(T, H))
+    cu = torch.tensor(cuts, dtype=torch.int32, device=dev)
+    P = len(cuts) - 1
+    M, St = kda.kcp_summaries(None, k, v, g, beta, cu)
+    _, St2 = kda.chunk_fwd(None, k, v, g, beta, cu_seqlens=cu, output=False)
+    eye = torch.eye(d, device=dev).expand(P, H, d, d).contiguous()
+    _, M2 = kda.chunk_fwd(None, k, None, g, beta, initial_state=eye, cu_seqlens=cu, output=False)
+    torch.cuda.synchronize()
+    assert torch.equal(M, M2) and torch.equal(St, St2)
+    kn, gn, bn = _np(k), _np(g), _np(beta)
+    tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    for s_ in range(P):
+        a, b = cuts[s_], cuts[s_ + 1]
+        for h in range(H):
+            m_ref = L.transition_product(kn[a:b, h], gn[a:b, h], bn[a:b, h])
+            assert _rel(_np(M[s_, h]), m_ref) <= tol, (s_, h)
+    print(f"[parity] KCP summaries {dtype} d={d}: one launch == two launches", flush=True)
+
+
 def test_kcp_segments_compose_to_the_whole_sequence():
     H, d = 4, 128
     cuts = [0, 500, 501, 621, 2048]
