@@ -180,6 +180,48 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                      "frac": _gbs(fb, ms) / HBM_PEAK_GBS,
                      "traffic": _traffic("kda_prefill.hip", "k3_prefill_8k_fused_prologue"),
                      "kernel": "kda::prefill_kernel<..., fused prologue>", "bytes_per_launch": fb}}
+    # the same prefill from raw inputs by the other routes: the front end as a
+    # pass of its own (L2Norm and gate), then the plain prefill ("unfused");
+    # a pass for L2Norm only, then the prefill with the gate fused ("split")
+    qn, kn = torch.empty_like(li["q_raw"]), torch.empty_like(li["k_raw"])
+    gn = torch.empty(li["z"].shape, dtype=torch.float32, device=dev)
+    of = torch.empty_like(x["v"])
+    sff = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+    def fe_all():
+        kda.front_end(li["q_raw"], li["k_raw"], li["z"], li["A_log"], li["b_alpha"], q=qn, k=kn, g=gn)
+
+    def fe_norm():
+        kda.front_end(li["q_raw"], li["k_raw"], q=qn, k=kn)
+
+    ms_fe, _ = time_launches(fe_all, args.steps, args.warmup, torch)
+    ms_fn, _ = time_launches(fe_norm, args.steps, args.warmup, torch)
+
+    def unfused():
+        fe_all()
+        kda.chunk_fwd(qn, kn, x["v"], gn, x["beta"], x["initial_state"], x["cu_seqlens"],
+                      chunk_size=w.chunk, out=of, final_state=sff)
+
+    def split():
+        fe_norm()
+        kda.chunk_fwd_fused(qn, kn, x["v"], li["z"], li["A_log"], li["b_alpha"], x["beta"],
+                            x["initial_state"], x["cu_seqlens"], l2norm=False, out=of,
+                            final_state=sff)
+
+    ms_un, _ = time_launches(unfused, args.steps, args.warmup, torch)
+    ms_sp, _ = time_launches(split, args.steps, args.warmup, torch)
+    el = n_tok * w.H * w.dk
+    feb, fnb = el * (3 * e + 2 * e + 4), el * 4 * e
+    res["front_end"] = {
+        "workload": w.name,
+        "fused_ms": res["prefill_fused_prologue"]["ms_per_step"],
+        "unfused_ms": ms_un, "split_ms": ms_sp,
+        "pass_l2norm_gate": {"ms": ms_fe, "GB/s": _gbs(feb, ms_fe), "bytes_per_launch": feb,
+                             "frac": _gbs(feb, ms_fe) / HBM_PEAK_GBS},
+        "pass_l2norm": {"ms": ms_fn, "GB/s": _gbs(fnb, ms_fn), "bytes_per_launch": fnb,
+                        "frac": _gbs(fnb, ms_fn) / HBM_PEAK_GBS},
+        "kernel": "kda::front_end_kernel"}
+    del qn, kn, gn, of, sff
     # the prefill with its attention output in fp32 (kda_chunk_fwd_ex)
     o32 = torch.empty(x["v"].shape, dtype=torch.float32, device=dev)
     sf32 = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)

@@ -272,6 +272,46 @@ kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void 
                                float *final_state, void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Steps of the front end done inside the prefill (kda_chunk_fwd_fused_ex). */
+#define KDA_FUSE_GATE 1   /* z, A_log, b_alpha replace g (the bounded gate) */
+#define KDA_FUSE_L2NORM 2 /* q, k arrive unnormalised (L2Norm in the kernel) */
+
+/*
+ * kda_chunk_fwd_fused with a choice of the front-end steps done in the
+ * kernel: fuse = KDA_FUSE_GATE | KDA_FUSE_L2NORM is kda_chunk_fwd_fused;
+ * fuse = KDA_FUSE_GATE takes q and k already L2-normalised (for instance by
+ * kda_front_end with g = NULL) and fuses only the bounded gate.  Any other
+ * value: KDA_ERR_UNSUPPORTED.  The row norms are reductions across the
+ * channels that the kernel's elementwise layout spreads over four waves; in
+ * the kernel they cost more than the separate normalisation pass, while the
+ * gate, elementwise per channel, costs less in the kernel than its fp32 g
+ * stream does outside.  Arguments, layouts and errors as kda_chunk_fwd_fused.
+ */
+kda_status kda_chunk_fwd_fused_ex(const void *q, const void *k, const void *v, const void *z,
+                                  const float *A_log, const float *b_alpha, const float *beta,
+                                  const float *initial_state, const int32_t *cu_seqlens,
+                                  int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
+                                  int32_t d_v, int32_t chunk_size, kda_dtype dtype, int32_t fuse,
+                                  void *o, float *final_state, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The layer's front end as a pass of its own (the unfused alternative to
+ * kda_chunk_fwd_fused): per (token, head) row of d elements
+ *     q = L2Norm(q_raw), k = L2Norm(k_raw)   (a zero row stays zero)
+ *     g = g_min sigma(e^{A_h} (z + b_alpha^h)), g_min = -5    when g != NULL
+ * (page "Notations mathematiques", function table "L2Norm" and rows q_t, k_t;
+ * "Glossaire", entry "Decroissance bornee"; notation table rows A_h,
+ * b_alpha^h, z_t).  Bound by HBM bandwidth.
+ *   q_raw, k_raw, z  [total_tokens][H][d] dtype     (z may be NULL if g is)
+ *   A_log [H], b_alpha [H][d] fp32                   (NULL if g is)
+ *   q, k  [total_tokens][H][d] dtype out; g [total_tokens][H][d] fp32 out or NULL
+ * d in {32, 64, 128}.  Outputs must not alias inputs.  One launch on `stream`.
+ */
+kda_status kda_front_end(const void *q_raw, const void *k_raw, const void *z, const float *A_log,
+                         const float *b_alpha, int64_t total_tokens, int32_t H, int32_t d,
+                         kda_dtype dtype, void *q, void *k, float *g, hipStream_t stream);
+
 /*
  * Output epilogue of the KDA layer: out = RMSNorm(o~) (.) sigma(gate), per row
  * (token, head) over d_v, RMSNorm(x) = x / sqrt(mean(x^2) + eps) (.) weight

@@ -6,7 +6,8 @@ declared in ``include/kda.h``).  This package only marshals arguments:
 per request), ``chunk_fwd_static`` (the prefill on a static device scratch,
 for callers that cannot allocate), plus the layer steps around them:
 ``chunk_fwd_fused`` (prefill with L2Norm and the bounded gate in the kernel),
-``step_decode_gated`` (decode with the output gate in the kernel), ``output_gate``,
+``step_decode_gated`` (decode with the output gate in the kernel),
+``front_end`` (L2Norm and the bounded gate as a pass of their own), ``output_gate``,
 ``short_conv``, ``state_compose`` and the segment helpers ``kcp_summaries`` /
 ``kcp_scan``.  The library is loaded on first use and its absence is an error.
 """
@@ -14,8 +15,8 @@ from . import inputs  # noqa: F401  (seeded synthetic inputs; no compute)
 
 _API = ("chunk_fwd", "step_decode", "chunk_fwd_fused", "output_gate", "short_conv",
         "state_compose", "kcp_summaries", "kcp_scan", "step_decode_gated", "chunk_fwd_static",
-        "library", "workspace_size", "KdaError")
-__all__ = list(_API[:10]) + ["inputs", "library"]
+        "front_end", "library", "workspace_size", "KdaError")
+__all__ = list(_API[:11]) + ["inputs", "library"]
 
 
 def __getattr__(name):

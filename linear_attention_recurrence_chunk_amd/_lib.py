@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_FUSE_GATE, KDA_FUSE_L2NORM = 1, 2
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 # prefill algorithms (kda_algo)
 ALGOS = {"auto": 0, "fused": 1, "two_pass": 2}
@@ -69,6 +70,11 @@ def library() -> ctypes.CDLL:
     lib.kda_segment_scan.restype = i32
     lib.kda_kcp_summaries.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp]
     lib.kda_kcp_summaries.restype = i32
+    lib.kda_chunk_fwd_fused_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                           i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_fused_ex.restype = i32
+    lib.kda_front_end.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.kda_front_end.restype = i32
     lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                         i32, i32, i32, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd_fused.restype = i32
@@ -344,12 +350,15 @@ def chunk_fwd_fused(q_raw: torch.Tensor, k_raw: torch.Tensor, v: torch.Tensor, z
                     A_log: torch.Tensor, b_alpha: torch.Tensor, beta: torch.Tensor,
                     initial_state: Optional[torch.Tensor] = None,
                     cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
-                    output_final_state: bool = True
+                    output_final_state: bool = True, l2norm: bool = True,
+                    out: Optional[torch.Tensor] = None,
+                    final_state: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Prefill with the fused front end (kda_chunk_fwd_fused): q, k are
-    L2-normalised in the kernel and g = -5 sigma(e^{A_h} (z + b_alpha^h)).
-    q_raw, k_raw, z like q of chunk_fwd (same dtype); A_log [H] fp32;
-    b_alpha [H, d_k] fp32; the rest as chunk_fwd."""
+    """Prefill with the front end fused in (kda_chunk_fwd_fused_ex):
+    g = -5 sigma(e^{A_h} (z + b_alpha^h)) in the kernel, and with l2norm=True
+    q, k L2-normalised there too (else q_raw, k_raw must be normalised
+    already, e.g. by front_end).  q_raw, k_raw, z like q of chunk_fwd (same
+    dtype); A_log [H] fp32; b_alpha [H, d_k] fp32; the rest as chunk_fwd."""
     if q_raw.dtype not in _DTYPES:
         raise ValueError(f"q_raw must be bf16 or fp32, got {q_raw.dtype}")
     dev = q_raw.device
@@ -374,14 +383,54 @@ def chunk_fwd_fused(q_raw: torch.Tensor, k_raw: torch.Tensor, v: torch.Tensor, z
         _need(initial_state, "initial_state", dtype=torch.float32, device=dev)
         if tuple(initial_state.shape) != sshape:
             raise ValueError(f"initial_state must have shape {sshape}")
-    out = torch.empty_like(v)
-    final_state = torch.empty(sshape, dtype=torch.float32, device=dev) if output_final_state else None
-    st = library().kda_chunk_fwd_fused(
+    out = _out(out, v.shape, v.dtype, dev)
+    if output_final_state:
+        final_state = _out(final_state, sshape, torch.float32, dev, "final_state")
+    else:
+        final_state = None
+    fuse = KDA_FUSE_GATE | (KDA_FUSE_L2NORM if l2norm else 0)
+    st = library().kda_chunk_fwd_fused_ex(
         _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(z), _ptr(A_log), _ptr(b_alpha), _ptr(beta),
         _ptr(initial_state), _ptr(cu_seqlens), num_seqs, n_tok, H, dk, dv, chunk_size,
-        _DTYPES[q_raw.dtype], _ptr(out), _ptr(final_state), None, 0, _stream(dev))
-    _check("kda_chunk_fwd_fused", st)
+        _DTYPES[q_raw.dtype], fuse, _ptr(out), _ptr(final_state), None, 0, _stream(dev))
+    _check("kda_chunk_fwd_fused_ex", st)
     return out, final_state
+
+
+def front_end(q_raw: torch.Tensor, k_raw: torch.Tensor, z: Optional[torch.Tensor] = None,
+              A_log: Optional[torch.Tensor] = None, b_alpha: Optional[torch.Tensor] = None,
+              q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
+              g: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """The front end as a pass of its own (kda_front_end): q = L2Norm(q_raw),
+    k = L2Norm(k_raw) and, when z is given, the fp32 log-decay
+    g = -5 sigma(e^{A_h} (z + b_alpha^h)).  q_raw, k_raw, z [..., H, d]."""
+    if q_raw.dtype not in _DTYPES:
+        raise ValueError(f"q_raw must be bf16 or fp32, got {q_raw.dtype}")
+    dev = q_raw.device
+    _gpu(dev)
+    _need(q_raw, "q_raw", ndim=(3, 4))
+    _need(k_raw, "k_raw", dtype=q_raw.dtype, ndim=(q_raw.dim(),), device=dev)
+    if k_raw.shape != q_raw.shape:
+        raise ValueError("q_raw and k_raw must share a shape")
+    H, d = q_raw.shape[-2:]
+    n_tok = q_raw.numel() // (H * d)
+    if z is not None:
+        _need(z, "z", dtype=q_raw.dtype, device=dev)
+        _need(A_log, "A_log", dtype=torch.float32, ndim=(1,), device=dev)
+        _need(b_alpha, "b_alpha", dtype=torch.float32, ndim=(2,), device=dev)
+        if z.shape != q_raw.shape or tuple(A_log.shape) != (H,) or tuple(b_alpha.shape) != (H, d):
+            raise ValueError("z like q_raw, A_log [H], b_alpha [H, d]")
+        g = _out(g, q_raw.shape, torch.float32, dev, "g")
+    else:
+        g = None
+    q = _out(q, q_raw.shape, q_raw.dtype, dev, "q")
+    k = _out(k, q_raw.shape, q_raw.dtype, dev, "k")
+    st = library().kda_front_end(_ptr(q_raw), _ptr(k_raw), _ptr(z), _ptr(A_log), _ptr(b_alpha),
+                                 n_tok, H, d, _DTYPES[q_raw.dtype], _ptr(q), _ptr(k), _ptr(g),
+                                 _stream(dev))
+    _check("kda_front_end", st)
+    return q, k, g
 
 
 def output_gate(o_raw: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor,

@@ -22,7 +22,10 @@ hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void
                                 const void *z, const float *A_log, const float *b_alpha,
                                 const float *beta, const float *s0, const int32_t *cu,
                                 int num_seqs, int64_t seq_len, int H, int d, int chunk,
-                                bool is_bf16, void *o, float *sf, hipStream_t stream);
+                                bool is_bf16, bool norm, void *o, float *sf, hipStream_t stream);
+hipError_t launch_front_end(const void *q_raw, const void *k_raw, const void *z, const float *A_log,
+                            const float *b_alpha, void *q, void *k, float *g, int64_t rows, int H,
+                            int d, bool is_bf16, hipStream_t stream);
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
                          const float *beta, float *state, void *o, int64_t NH, int d,
                          bool is_bf16, const void *gate, const float *gw, float eps, void *out,
@@ -220,6 +223,33 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                             workspace_bytes, stream);
 }
 
+kda_status kda_chunk_fwd_fused_ex(const void *q, const void *k, const void *v, const void *z,
+                                  const float *A_log, const float *b_alpha, const float *beta,
+                                  const float *initial_state, const int32_t *cu_seqlens,
+                                  int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t d_k,
+                                  int32_t d_v, int32_t chunk_size, kda_dtype dtype, int32_t fuse,
+                                  void *o, float *final_state, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream)
+{
+    if (fuse != (KDA_FUSE_GATE | KDA_FUSE_L2NORM) && fuse != KDA_FUSE_GATE)
+        return KDA_ERR_UNSUPPORTED;
+    // z stands in for g in the common checks (same shape and alignment rule)
+    const kda_status st =
+        prefill_check(q, k, v, reinterpret_cast<const float *>(z), beta, initial_state,
+                      cu_seqlens, num_seqs, total_tokens, H, d_k, d_v, chunk_size, dtype,
+                      KDA_ALGO_FUSED, o, final_state, workspace, workspace_bytes, false);
+    if (st != KDA_OK) return st;
+    if (total_tokens > 0 && (!A_log || !b_alpha)) return KDA_ERR_NULL;
+    if (misaligned(A_log) || misaligned(b_alpha)) return KDA_ERR_ALIGN;
+    if (num_seqs == 0) return KDA_OK;
+    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
+    const hipError_t e = kda::launch_prefill_fused(q, k, v, z, A_log, b_alpha, beta, initial_state,
+                                                   cu_seqlens, num_seqs, seq_len, H, d_k, 64,
+                                                   dtype == KDA_BF16, (fuse & KDA_FUSE_L2NORM) != 0,
+                                                   o, final_state, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void *v, const void *z,
                                const float *A_log, const float *b_alpha, const float *beta,
                                const float *initial_state, const int32_t *cu_seqlens,
@@ -228,20 +258,27 @@ kda_status kda_chunk_fwd_fused(const void *q_raw, const void *k_raw, const void 
                                float *final_state, void *workspace, size_t workspace_bytes,
                                hipStream_t stream)
 {
-    // z stands in for g in the common checks (same shape and alignment rule)
-    const kda_status st =
-        prefill_check(q_raw, k_raw, v, reinterpret_cast<const float *>(z), beta, initial_state,
-                      cu_seqlens, num_seqs, total_tokens, H, d_k, d_v, chunk_size, dtype,
-                      KDA_ALGO_FUSED, o, final_state, workspace, workspace_bytes, false);
-    if (st != KDA_OK) return st;
-    if (total_tokens > 0 && (!A_log || !b_alpha)) return KDA_ERR_NULL;
-    if (misaligned(A_log) || misaligned(b_alpha)) return KDA_ERR_ALIGN;
-    if (num_seqs == 0) return KDA_OK;
-    const int64_t seq_len = cu_seqlens ? 0 : total_tokens / num_seqs;
-    const hipError_t e = kda::launch_prefill_fused(q_raw, k_raw, v, z, A_log, b_alpha, beta,
-                                                   initial_state, cu_seqlens, num_seqs, seq_len,
-                                                   H, d_k, 64, dtype == KDA_BF16, o, final_state,
-                                                   stream);
+    return kda_chunk_fwd_fused_ex(q_raw, k_raw, v, z, A_log, b_alpha, beta, initial_state,
+                                  cu_seqlens, num_seqs, total_tokens, H, d_k, d_v, chunk_size,
+                                  dtype, KDA_FUSE_GATE | KDA_FUSE_L2NORM, o, final_state,
+                                  workspace, workspace_bytes, stream);
+}
+
+kda_status kda_front_end(const void *q_raw, const void *k_raw, const void *z, const float *A_log,
+                         const float *b_alpha, int64_t total_tokens, int32_t H, int32_t d,
+                         kda_dtype dtype, void *q, void *k, float *g, hipStream_t stream)
+{
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens < 0 || H < 1 || d < 1) return KDA_ERR_SHAPE;
+    if (!head_size_ok(d)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens == 0) return KDA_OK;
+    if (!q_raw || !k_raw || !q || !k) return KDA_ERR_NULL;
+    if (g && (!z || !A_log || !b_alpha)) return KDA_ERR_NULL;
+    if (misaligned(q_raw) || misaligned(k_raw) || misaligned(z) || misaligned(A_log) ||
+        misaligned(b_alpha) || misaligned(q) || misaligned(k) || misaligned(g))
+        return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_front_end(q_raw, k_raw, z, A_log, b_alpha, q, k, g,
+                                               total_tokens * H, H, d, dtype == KDA_BF16, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -6,11 +6,14 @@
 //   - ShortConv: causal depthwise convolution with 4 taps and a streaming state
 //     (function table "ShortConv", "Glossaire" entry "ShortConv", model table
 //     "ShortConv kernel (KDA) 4");
+//   - the front end, unfused: L2Norm of q and k and the bounded gate
+//     ("Glossaire", entry "Decroissance bornee"; function table "L2Norm");
 //   - state composition for context-parallel segments: S_out = M S_in + S~
 //     ("Glossaire", entry "KCP"; notation table rows M_t and S~), one step
 //     over a batch, or the whole scan over P segments in one launch.
-// The first two are elementwise and bound by HBM bandwidth: coalesced accesses
-// (16-byte lanes for the gate, 8-byte for ShortConv), fp32 arithmetic.  The
+// The first three are elementwise and bound by HBM bandwidth: coalesced
+// accesses (16-byte lanes for the gate and the front end, 8-byte for
+// ShortConv), fp32 arithmetic.  The
 // composition is a batch of dense fp32 products on the matrix cores
 // (v_mfma_f32_16x16x4_f32).
 #include "kda_common.hpp"
@@ -109,6 +112,137 @@ hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *
     return out_f32 ? launch_output_gate_d<bf16, bf16, float>(KDA_OG_ARGS)
                    : launch_output_gate_d<bf16, bf16, bf16>(KDA_OG_ARGS);
 #undef KDA_OG_ARGS
+}
+
+// ---------------------------------------------------------------------------
+// Front end of the recurrence, unfused: L2Norm of the q and k rows (function
+// table "L2Norm"; a zero row maps to zero) and, when asked for, the bounded
+// gate's log-decay g = g_min sigma(e^{A_h} (z + b_alpha^h)) ("Glossaire",
+// entry "Decroissance bornee", with the per-head bias of the notation table),
+// g_min = -5.  One row = one (token, head); a lane holds 16 bytes of q and of
+// k, the LPR lanes of a row reduce the sums of squares with xor shuffles.
+template <typename T, int D, bool GATE>
+__global__ __launch_bounds__(256) void front_end_kernel(const T *__restrict__ q_raw,
+                                                        const T *__restrict__ k_raw,
+                                                        const T *__restrict__ z,
+                                                        const float *__restrict__ A_log,
+                                                        const float *__restrict__ b_alpha,
+                                                        T *__restrict__ q, T *__restrict__ k,
+                                                        float *__restrict__ g, int64_t rows, int H)
+{
+    constexpr int EPL = 16 / (int)sizeof(T);     // elements per lane
+    constexpr int LPR = D / EPL;                 // lanes per row
+    constexpr int RPB = 256 / LPR;               // rows per block and step
+    constexpr int U = 1;                         // rows per thread and step (2 measured slower)
+    static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row mapping");
+    typedef T vec __attribute__((ext_vector_type(EPL)));
+    const int t = threadIdx.x, c0 = (t % LPR) * EPL;
+    const int64_t step = (int64_t)gridDim.x * RPB;          // between a thread's rows
+    int64_t row = (int64_t)blockIdx.x * RPB + t / LPR;
+    // the head of a row, advanced without a 64-bit division per row
+    int h = (int)(row % H);
+    const int hstep = (int)(step % H);
+    const auto adv = [&](int x) { x += hstep; return x >= H ? x - H : x; };
+    for (; row < rows; row += U * step) {
+        vec xq[U], xk[U], xz[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = row + u * step;
+            if (r < rows) {
+                xq[u] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(q_raw + r * D + c0));
+                xk[u] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(k_raw + r * D + c0));
+                if (GATE) xz[u] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(z + r * D + c0));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = row + u * step;
+            const int hu = h;
+            h = adv(h);
+            if (r >= rows) continue;
+            float fq[EPL], fk[EPL], sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                fq[e] = to_f32(xq[u][e]);
+                fk[e] = to_f32(xk[u][e]);
+                sq += fq[e] * fq[e];
+                sk += fk[e] * fk[e];
+            }
+#pragma unroll
+            for (int m = 1; m < LPR; m <<= 1) {
+                sq += __shfl_xor(sq, m);
+                sk += __shfl_xor(sk, m);
+            }
+            const float iq = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
+            const float ik = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
+            vec yq, yk;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                yq[e] = from_f32<T>(fq[e] * iq);
+                yk[e] = from_f32<T>(fk[e] * ik);
+            }
+            *reinterpret_cast<vec *>(q + r * D + c0) = yq;
+            *reinterpret_cast<vec *>(k + r * D + c0) = yk;
+            if (GATE) {
+                const float eA = __expf(A_log[hu]);
+                const float *bb = b_alpha + (int64_t)hu * D + c0;
+#pragma unroll
+                for (int e4 = 0; e4 < EPL; e4 += 4) {
+                    f32x4 y;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = eA * (to_f32(xz[u][e4 + i]) + bb[e4 + i]);
+                        y[i] = -5.f * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+                    }
+                    *reinterpret_cast<f32x4 *>(g + r * D + c0 + e4) = y;
+                }
+            }
+        }
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_front_end_t(const void *q_raw, const void *k_raw, const void *z,
+                                     const float *A_log, const float *b_alpha, void *q, void *k,
+                                     float *g, int64_t rows, int H, hipStream_t stream)
+{
+    constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
+    const int64_t need = (rows + RPB - 1) / RPB;
+    const int64_t blocks = need < 1024 ? need : 1024;
+    if (g)
+        hipLaunchKernelGGL((front_end_kernel<T, D, true>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, (const T *)q_raw, (const T *)k_raw, (const T *)z, A_log, b_alpha,
+                           (T *)q, (T *)k, g, rows, H);
+    else
+        hipLaunchKernelGGL((front_end_kernel<T, D, false>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, (const T *)q_raw, (const T *)k_raw, (const T *)nullptr,
+                           (const float *)nullptr, (const float *)nullptr, (T *)q, (T *)k,
+                           (float *)nullptr, rows, H);
+    return hipGetLastError();
+}
+
+// rows = tokens x H; g == NULL: L2Norm only.
+hipError_t launch_front_end(const void *q_raw, const void *k_raw, const void *z, const float *A_log,
+                            const float *b_alpha, void *q, void *k, float *g, int64_t rows, int H,
+                            int d, bool is_bf16, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+#define KDA_FE_ARGS q_raw, k_raw, z, A_log, b_alpha, q, k, g, rows, H, stream
+    if (is_bf16) {
+        switch (d) {
+            case 32: return launch_front_end_t<bf16, 32>(KDA_FE_ARGS);
+            case 64: return launch_front_end_t<bf16, 64>(KDA_FE_ARGS);
+            case 128: return launch_front_end_t<bf16, 128>(KDA_FE_ARGS);
+        }
+    } else {
+        switch (d) {
+            case 32: return launch_front_end_t<float, 32>(KDA_FE_ARGS);
+            case 64: return launch_front_end_t<float, 64>(KDA_FE_ARGS);
+            case 128: return launch_front_end_t<float, 128>(KDA_FE_ARGS);
+        }
+    }
+#undef KDA_FE_ARGS
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

@@ -175,8 +175,14 @@ __device__ __forceinline__ V load_at(const E *base, uint32_t byte_off)
 // the next chunk's loads can be spread over the phases of the current one.
 enum { LOAD_G = 1, LOAD_KQ = 2, LOAD_VB = 4, LOAD_ALL = 7 };
 
+// The layer's front end inside the kernel (template argument FUSED): none (q,
+// k and g given), the bounded gate and the L2Norm of q and k (raw q, k and
+// decay logits z given), or the bounded gate only (q, k given L2-normalised,
+// z instead of g).
+enum { FE_NONE = 0, FE_GATE_NORM = 1, FE_GATE = 2 };
+
 // OUT = false (state only): q is not read.  v == nullptr: the values are zero.
-template <bool FUSED, bool OUT, typename T, int DK, int BV>
+template <int FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void load_chunk(ChunkRegs<T, DK, BV> &R, int parts, const SeqView &sv,
                                            int64_t t0, const T *__restrict__ q,
                                            const T *__restrict__ k, const T *__restrict__ v,
@@ -291,7 +297,7 @@ __device__ __forceinline__ float bounded_alpha(float z, float eA, float b)
 // chunk lies in the sequence.  FUSED: g comes from decay logits through the
 // bounded gate, and k and q are divided by their row norms (L2Norm of the
 // function table), whose partial sums of squares are in sm.nrm.
-template <bool FULL, bool FUSED, bool OUT, typename T, int DK, int BV>
+template <bool FULL, int FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
                                         const GateCtx &gc, bool pre)
 {
@@ -345,7 +351,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
             const bool in = FULL || r0 + r < nv;
             // fused prologue: 1 / ||k_r||, 1 / ||q_r|| (0 for a zero row)
             float ik = 1.f, iq = 1.f;
-            if (FUSED) {
+            if (FUSED == FE_GATE_NORM) {
                 float s2k = 0.f, s2q = 0.f;
 #pragma unroll
                 for (int w = 0; w < Cf::WPB; ++w) {
@@ -360,7 +366,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
             for (int cc = 0; cc < 2; ++cc) {
                 kk[cc] = in ? to_f32(R.k[r][cc]) : 0.f;
                 qq[cc] = (OUT && in) ? to_f32(R.q[r][cc]) : 0.f;
-                if (FUSED) {
+                if (FUSED == FE_GATE_NORM) {
                     kk[cc] *= ik;
                     qq[cc] *= iq;
                 }
@@ -388,7 +394,7 @@ __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, 
     }
 }
 
-template <bool FUSED, bool OUT, typename T, int DK, int BV>
+template <int FUSED, bool OUT, typename T, int DK, int BV>
 __device__ __forceinline__ void e_phase(Smem<T, DK, BV> &sm, const ChunkRegs<T, DK, BV> &R, int nv,
                                         const GateCtx &gc, bool pre = false)
 {
@@ -727,8 +733,9 @@ __device__ __forceinline__ void diag_inverse(Smem<T, DK, BV> &sm, int I, const f
     *reinterpret_cast<V4 *>(&sm.Tm[I][n16][4 * grp]) = PT::to_quad(Da);
 }
 
-// FUSED: q and k arrive unnormalised and g is replaced by decay logits z with
-// the per-head gate parameters A_log [H] and b_alpha [H][DK].  OUT = false:
+// FUSED (FE_GATE, FE_GATE_NORM): g is replaced by decay logits z with the
+// per-head gate parameters A_log [H] and b_alpha [H][DK]; with FE_GATE_NORM q
+// and k also arrive unnormalised.  OUT = false:
 // only the final state is computed (no o, q not read, and neither P nor
 // (Q o e^G) S is formed); v == nullptr stands for zero values.  TO: the type
 // of o (the input type, or fp32 for bf16 inputs).
@@ -737,7 +744,7 @@ __device__ __forceinline__ void diag_inverse(Smem<T, DK, BV> &sm, int I, const f
 // those of the first half run the transition product, from S = I with zero
 // values, and write M to mfinal; those of the second half run from S = 0 with
 // the values and write S~ to sfinal.  s0 is not read.
-template <typename T, int DK, int BV, int DV, bool FUSED, bool OUT, typename TO, bool KCP = false>
+template <typename T, int DK, int BV, int DV, int FUSED, bool OUT, typename TO, bool KCP = false>
 __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
@@ -850,7 +857,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     ChunkRegs<T, DK, BV> R;
     if (nchunks > 0) {
         load_chunk<FUSED, OUT>(R, LOAD_ALL, sv, sv.bos, q, k, vsrc, g, z, beta, DV);
-        if (FUSED) {
+        if (FUSED == FE_GATE_NORM) {
             norm_partials(sm, R);
             __syncthreads();
         }
@@ -967,7 +974,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
             }
         }
         // fused prologue: the next chunk's row norms, read by its E after B2
-        if (FUSED && more) norm_partials(sm, R);
+        if (FUSED == FE_GATE_NORM && more) norm_partials(sm, R);
         // fused prologue: the state waves take their items' gate ahead
         const bool pre = FUSED && state_wave && wv < Cf::EWAVES;
         if (pre && more) gate_items(sm, R, gc);
@@ -1075,7 +1082,7 @@ __global__ __launch_bounds__(1024, 1) void prefill_kernel(
     }
 }
 
-template <typename T, int D, int BV, bool FUSED, bool OUT, typename TO>
+template <typename T, int D, int BV, int FUSED, bool OUT, typename TO>
 static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *s0, const int32_t *cu,
                                    int num_seqs, int64_t seq_len, int H, void *o, float *sf,
@@ -1102,7 +1109,7 @@ static hipError_t launch_kcp_t(const void *k, const void *v, const float *g, con
     const int64_t nwork = (int64_t)num_seqs * H * (2 * D / BV);
     if (nwork == 0) return hipSuccess;
     if ((int64_t)H * D * 4 >= (int64_t)1 << 24) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, false, false, T, true>), dim3((unsigned)nwork),
+    hipLaunchKernelGGL((prefill_kernel<T, D, BV, D, FE_NONE, false, T, true>), dim3((unsigned)nwork),
                        dim3(Cfg<T, D, BV>::NT), 0, stream, (const T *)nullptr, (const T *)k,
                        (const T *)v, g, beta, (const float *)nullptr, cu, num_seqs, seq_len, H,
                        (T *)nullptr, St, (const T *)nullptr, (const float *)nullptr,
@@ -1132,7 +1139,7 @@ hipError_t launch_kcp_summaries(const void *k, const void *v, const float *g, co
 }
 
 // O32: o in fp32 for bf16 inputs (only the unfused kernel with an output).
-template <bool FUSED, bool OUT, bool O32>
+template <int FUSED, bool OUT, bool O32>
 static hipError_t launch_prefill_f(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *s0, const int32_t *cu,
                                    int num_seqs, int64_t seq_len, int H, int d, bool is_bf16,
@@ -1164,28 +1171,33 @@ hipError_t launch_prefill(const void *q, const void *k, const void *v, const flo
 {
     if (chunk != 64) return hipErrorInvalidValue;
     if (!o)   // state only
-        return launch_prefill_f<false, false, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H,
+        return launch_prefill_f<FE_NONE, false, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H,
                                                      d, is_bf16, o, sf, nullptr, nullptr, nullptr,
                                                      stream);
     if (is_bf16 && o_f32)
-        return launch_prefill_f<false, true, true>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
+        return launch_prefill_f<FE_NONE, true, true>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
                                                    is_bf16, o, sf, nullptr, nullptr, nullptr,
                                                    stream);
-    return launch_prefill_f<false, true, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
+    return launch_prefill_f<FE_NONE, true, false>(q, k, v, g, beta, s0, cu, num_seqs, seq_len, H, d,
                                                 is_bf16, o, sf, nullptr, nullptr, nullptr, stream);
 }
 
+// norm: q, k arrive unnormalised (FE_GATE_NORM), else normalised (FE_GATE).
 hipError_t launch_prefill_fused(const void *q_raw, const void *k_raw, const void *v,
                                 const void *z, const float *A_log, const float *b_alpha,
                                 const float *beta, const float *s0, const int32_t *cu,
                                 int num_seqs, int64_t seq_len, int H, int d, int chunk,
-                                bool is_bf16, void *o, float *sf, hipStream_t stream)
+                                bool is_bf16, bool norm, void *o, float *sf, hipStream_t stream)
 {
     if (chunk != 64) return hipErrorInvalidValue;
     if (!o) return hipErrorInvalidValue;
-    return launch_prefill_f<true, true, false>(q_raw, k_raw, v, nullptr, beta, s0, cu, num_seqs,
-                                               seq_len, H, d, is_bf16, o, sf, z, A_log, b_alpha,
-                                               stream);
+    if (norm)
+        return launch_prefill_f<FE_GATE_NORM, true, false>(q_raw, k_raw, v, nullptr, beta, s0, cu,
+                                                           num_seqs, seq_len, H, d, is_bf16, o, sf,
+                                                           z, A_log, b_alpha, stream);
+    return launch_prefill_f<FE_GATE, true, false>(q_raw, k_raw, v, nullptr, beta, s0, cu, num_seqs,
+                                                  seq_len, H, d, is_bf16, o, sf, z, A_log, b_alpha,
+                                                  stream);
 }
 
 }  // namespace kda

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                             "kda_chunk_fwd_ex", "kda_output_gate_ex", "kda_chunk_fwd_algo",
                             "kda_chunk_fwd_algo_workspace_size", "kda_chunk_fwd_two_pass_static",
                             "kda_chunk_fwd_static_scratch_bytes", "kda_step_decode_gated", "kda_segment_scan",
-                            "kda_kcp_summaries"])
+                            "kda_kcp_summaries", "kda_chunk_fwd_fused_ex", "kda_front_end"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -291,6 +291,15 @@ def test_chunk_fwd_fused_rejects(kw, status):
 
 
 @gpu_visible
+@pytest.mark.parametrize("fuse", [0, 2, 4, -1])
+def test_chunk_fwd_fused_ex_rejects_unknown_steps(fuse):
+    p = ctypes.c_void_p
+    assert _lib.library().kda_chunk_fwd_fused_ex(
+        p(A), p(A), p(A), p(A), p(A), p(A), p(A), None, None, 1, 128, 2, 64, 64, 64, 1, fuse,
+        p(A), None, None, 0, None) == EUNSUP
+
+
+@gpu_visible
 def test_layer_steps_reject():
     lib = _lib.library()
     p = ctypes.c_void_p
@@ -321,6 +330,14 @@ def test_layer_steps_reject():
     assert lib.kda_state_compose(p(A), None, p(A), p(A), 4, 64, 64, None) == ENULL
     assert lib.kda_state_compose(p(A), p(A), p(A), p(MIS), 4, 64, 64, None) == EALIGN
     assert lib.kda_state_compose(None, None, None, None, 0, 64, 64, None) == OK
+    # front end as a pass of its own
+    fe = lambda **kw: (lambda a: lib.kda_front_end(
+        a["qr"], a["kr"], a["z"], a["A"], a["b"], a["n"], 2, a["d"], a["dt"], a["q"], a["k"], a["g"],
+        None))({**dict(qr=p(A), kr=p(A), z=p(A), A=p(A), b=p(A), n=10, d=64, dt=1, q=p(A), k=p(A),
+                       g=p(A)), **kw})
+    assert fe(d=48) == EUNSUP and fe(dt=7) == EUNSUP and fe(n=-1) == ESHAPE
+    assert fe(qr=None) == ENULL and fe(k=None) == ENULL and fe(z=None) == ENULL
+    assert fe(g=p(MIS)) == EALIGN and fe(n=0, qr=None) == OK
     # segment summaries in one launch
     ks = lambda **kw: (lambda a: lib.kda_kcp_summaries(
         a["k"], a["v"], p(A), p(A), None, a["P"], a["n"], 2, a["d"], a["C"], a["dt"], a["M"], a["S"],

@@ -71,6 +71,63 @@ def test_fused_prologue_prefill(dtype, d, lens, state_std, tol):
     assert eo <= tol and es <= tol
 
 
+def _front_end_paths(mode, q_raw, k_raw, v, z, A_log, b_alpha, beta, cu, s0):
+    """The prefill from raw inputs by one of the two other routes: 'split' (a
+    front-end pass for L2Norm, the gate fused in the prefill) or 'unfused' (a
+    front-end pass for both, then the plain prefill)."""
+    if mode == "split":
+        q, k, _ = kda.front_end(q_raw, k_raw)
+        return kda.chunk_fwd_fused(q, k, v, z, A_log, b_alpha, beta, initial_state=s0,
+                                   cu_seqlens=cu, l2norm=False)
+    q, k, g = kda.front_end(q_raw, k_raw, z, A_log, b_alpha)
+    return kda.chunk_fwd(q, k, v, g, beta, s0, cu)
+
+
+@pytest.mark.parametrize("mode", ["split", "unfused"])
+@pytest.mark.parametrize("dtype,d,lens,state_std,tol", [
+    (torch.bfloat16, 128, [300], 0.0, 2e-2),
+    (torch.bfloat16, 128, [64, 1, 0, 129, 200], 0.05, 2e-2),
+    (torch.bfloat16, 64, [250, 63], 0.05, 2e-2),
+    (torch.bfloat16, 32, [333], 0.0, 2e-2),
+    (torch.float32, 32, [100, 0, 77, 256], 0.1, 1e-4),
+    (torch.float32, 64, [190], 0.1, 1e-4),
+])
+def test_front_end_routes(mode, dtype, d, lens, state_std, tol):
+    H = 3
+    args = _fused_inputs(lens, H, d, dtype, seed=d + len(lens), state_std=state_std)
+    o, sf = _front_end_paths(mode, *args)
+    torch.cuda.synchronize()
+    o_ref, s_ref = _fused_oracle(*args)
+    eo, es = _rel(_np(o), o_ref), _rel(_np(sf), s_ref)
+    print(f"[parity] front end {mode} {dtype} d={d} lens={lens}: o={eo:.3e}, state={es:.3e}")
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64),
+                                     (torch.bfloat16, 32), (torch.float32, 128),
+                                     (torch.float32, 64), (torch.float32, 32)])
+def test_front_end_pass_against_oracle(dtype, d):
+    H, T = 5, 203
+    args = _fused_inputs([T], H, d, dtype, seed=60 + d)
+    q_raw, k_raw, v, z, A_log, b_alpha = args[:6]
+    q_raw[17, 2] = 0                                  # a zero row stays zero
+    q, k, g = kda.front_end(q_raw, k_raw, z, A_log, b_alpha)
+    q2, k2, g2 = kda.front_end(q_raw, k_raw)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(q[17, 2]) == 0
+    qr, kr = L.l2norm(_np(q_raw)), L.l2norm(_np(k_raw))
+    gr = L.bounded_gate(_np(z), _np(A_log), _np(b_alpha))
+    # one rounding of the result: half an ulp of the dtype, relative
+    tq = 2 ** -8 if dtype == torch.bfloat16 else 1e-6
+    # the L2Norm-only pass: the same rows (the two instances may contract the
+    # sums of squares differently, so equal up to the same bound)
+    assert g2 is None
+    assert np.max(np.abs(_np(q2) - qr)) <= tq and np.max(np.abs(_np(k2) - kr)) <= tq
+    assert np.max(np.abs(_np(q) - qr)) <= tq and np.max(np.abs(_np(k) - kr)) <= tq
+    assert np.max(np.abs(_np(g) - gr)) <= 5 * 2 ** -20
+    print(f"[parity] front end pass {dtype} d={d}", flush=True)
+
+
 def test_fused_prologue_k3_8k_sampled_heads():
     H, d, T = 96, 128, 8192
     args = _fused_inputs([T], H, d, torch.bfloat16, seed=7)
@@ -81,6 +138,18 @@ def test_fused_prologue_k3_8k_sampled_heads():
     o_ref, s_ref = _fused_oracle(*args, heads=heads)
     eo, es = _rel(_np(o)[:, heads], o_ref), _rel(_np(sf)[:, heads], s_ref)
     print(f"[parity] fused prologue 8k x 96 heads {heads}: o={eo:.3e}, state={es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_front_end_split_k3_8k_sampled_heads():
+    H, d, T = 96, 128, 8192
+    args = _fused_inputs([T], H, d, torch.bfloat16, seed=7)
+    o, sf = _front_end_paths("split", *args)
+    torch.cuda.synchronize()
+    heads = [0, 95]
+    o_ref, s_ref = _fused_oracle(*args, heads=heads)
+    eo, es = _rel(_np(o)[:, heads], o_ref), _rel(_np(sf)[:, heads], s_ref)
+    print(f"[parity] split front end 8k x 96 heads {heads}: o={eo:.3e}, state={es:.3e}")
     assert eo <= 2e-2 and es <= 2e-2
 
 
