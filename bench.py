@@ -266,6 +266,33 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                                       "traffic": _traffic("kda_layer.hip", "short_conv_k3_8k"),
                                       "kernel": "kda::short_conv_kernel (+ state update)",
                                       "bytes_per_launch": cb}}
+    # the layer's q, k, v from their projections: ShortConv of each, then a
+    # pass for the L2Norm of q and k ("separate"), against ShortConv with the
+    # L2Norm in the same pass for q and k ("fused")
+    C3 = w.H * w.dk
+    xs = [li["q_raw"].view(n_tok, C3), li["k_raw"].view(n_tok, C3), x["v"].view(n_tok, C3)]
+    ys = [torch.empty_like(xs[0]) for _ in range(3)]
+    qn, kn = torch.empty_like(ys[0]), torch.empty_like(ys[1])
+    sts = [torch.zeros(n_seq, 3, C3, device=dev) for _ in range(3)]
+
+    def conv_sep():
+        for i in range(3):
+            kda.short_conv(xs[i], li["conv_w"], x["cu_seqlens"], sts[i], out=ys[i])
+        kda.front_end(ys[0].view(li["q_raw"].shape), ys[1].view(li["q_raw"].shape),
+                      q=qn.view(li["q_raw"].shape), k=kn.view(li["q_raw"].shape))
+
+    def conv_fused():
+        for i in range(3):
+            kda.short_conv(xs[i], li["conv_w"], x["cu_seqlens"], sts[i], out=ys[i],
+                           l2norm_d=w.dk if i < 2 else 0)
+
+    ms_cs, _ = time_launches(conv_sep, args.steps, args.warmup, torch)
+    ms_cf, _ = time_launches(conv_fused, args.steps, args.warmup, torch)
+    res["short_conv_l2norm"] = {"tokens": n_tok, "streams": 3, "separate_ms": ms_cs,
+                                "fused_ms": ms_cf,
+                                "fused_GB/s": _gbs(3 * cb, ms_cf),
+                                "kernel": "kda::short_conv_kernel<..., NORMD = d_k>"}
+    del xs, ys, qn, kn, sts
     del li, o, og, xc, st
     # context-parallel segments: the sequence split in P = 4 ("Glossaire",
     # entry "KCP").  Each of P devices would compute its segment's summaries,

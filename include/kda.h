@@ -372,6 +372,21 @@ kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_
                           float *conv_state, void *y, kda_dtype dtype, hipStream_t stream);
 
 /*
+ * kda_short_conv, then, with l2norm_d > 0, each output row of l2norm_d
+ * channels (one head) L2-normalised (function table "L2Norm"; a zero row stays
+ * zero; page "Notations mathematiques": q_t and k_t are the L2-normalised
+ * outputs of the ShortConv of their projections): the layer's q and k in one
+ * pass over the projections, with no separate normalisation pass.  The
+ * streaming state holds the convolution's inputs as in kda_short_conv.
+ * l2norm_d in {0, 32, 64, 128}, a divisor of channels (else
+ * KDA_ERR_UNSUPPORTED).  Everything else as kda_short_conv.
+ */
+kda_status kda_short_conv_ex(const void *x, const float *weight, const int32_t *cu_seqlens,
+                             int32_t num_seqs, int64_t total_tokens, int32_t channels,
+                             float *conv_state, void *y, kda_dtype dtype, int32_t l2norm_d,
+                             hipStream_t stream);
+
+/*
  * Composition of context-parallel segment summaries ("Glossaire", entry
  * "KCP"; notation table rows M_t and S~): for b < count,
  *     S_out[b] = M[b] S_in[b] + S_tilde[b]      (fp32 throughout).

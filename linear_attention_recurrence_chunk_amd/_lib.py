@@ -75,6 +75,8 @@ def library() -> ctypes.CDLL:
     lib.kda_chunk_fwd_fused_ex.restype = i32
     lib.kda_front_end.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.kda_front_end.restype = i32
+    lib.kda_short_conv_ex.argtypes = [vp, vp, vp, i32, i64, i32, vp, vp, i32, i32, vp]
+    lib.kda_short_conv_ex.restype = i32
     lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                         i32, i32, i32, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd_fused.restype = i32
@@ -474,11 +476,13 @@ def output_gate(o_raw: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor,
 
 
 def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
-               conv_state: Optional[torch.Tensor] = None, num_seqs: Optional[int] = None
-               ) -> torch.Tensor:
-    """Causal 4-tap depthwise convolution (kda_short_conv).  x [N_tok, C]
+               conv_state: Optional[torch.Tensor] = None, num_seqs: Optional[int] = None,
+               l2norm_d: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal 4-tap depthwise convolution (kda_short_conv_ex).  x [N_tok, C]
     (packed; one sequence, ``num_seqs`` equal ones, or cu_seqlens); weight
-    [C, 4] fp32; conv_state [N, 3, C] fp32 is read and updated in place."""
+    [C, 4] fp32; conv_state [N, 3, C] fp32 is read and updated in place.
+    l2norm_d > 0: each output row of l2norm_d channels (a head) is then
+    L2-normalised."""
     if x.dtype not in _DTYPES:
         raise ValueError(f"x must be bf16 or fp32, got {x.dtype}")
     dev = x.device
@@ -497,10 +501,11 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: Optional[torch
         _need(conv_state, "conv_state", dtype=torch.float32, device=dev)
         if tuple(conv_state.shape) != (nseq, 3, C):
             raise ValueError(f"conv_state must be {(nseq, 3, C)}")
-    y = torch.empty_like(x)
-    st = library().kda_short_conv(_ptr(x), _ptr(weight), _ptr(cu_seqlens), nseq, n_tok, C,
-                                  _ptr(conv_state), _ptr(y), _DTYPES[x.dtype], _stream(dev))
-    _check("kda_short_conv", st)
+    y = _out(out, x.shape, x.dtype, dev)
+    st = library().kda_short_conv_ex(_ptr(x), _ptr(weight), _ptr(cu_seqlens), nseq, n_tok, C,
+                                     _ptr(conv_state), _ptr(y), _DTYPES[x.dtype], int(l2norm_d),
+                                     _stream(dev))
+    _check("kda_short_conv_ex", st)
     return y
 
 

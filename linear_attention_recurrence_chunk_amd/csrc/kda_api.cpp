@@ -34,7 +34,7 @@ hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *
                               void *out, int64_t rows, int dv, bool is_bf16, bool in_f32,
                               bool out_f32, hipStream_t stream);
 hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, int nseq,
-                             int64_t ntok, int C, float *state, void *y, bool is_bf16,
+                             int64_t ntok, int C, float *state, void *y, bool is_bf16, int normd,
                              hipStream_t stream);
 hipError_t launch_compose(const float *M, const float *S_in, const float *S_tilde, float *S_out,
                           int64_t count, int d, hipStream_t stream);
@@ -310,13 +310,16 @@ kda_status kda_output_gate(const void *o_raw, const void *gate, const float *wei
     return kda_output_gate_ex(o_raw, dtype, gate, weight, eps, out, dtype, rows, d_v, dtype, stream);
 }
 
-kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,
-                          int32_t num_seqs, int64_t total_tokens, int32_t channels,
-                          float *conv_state, void *y, kda_dtype dtype, hipStream_t stream)
+kda_status kda_short_conv_ex(const void *x, const float *weight, const int32_t *cu_seqlens,
+                             int32_t num_seqs, int64_t total_tokens, int32_t channels,
+                             float *conv_state, void *y, kda_dtype dtype, int32_t l2norm_d,
+                             hipStream_t stream)
 {
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || total_tokens < 0 || channels < 1) return KDA_ERR_SHAPE;
     if (channels % 4 != 0) return KDA_ERR_UNSUPPORTED;
+    if (l2norm_d != 0 && (!head_size_ok(l2norm_d) || channels % l2norm_d != 0))
+        return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens != 0) return KDA_ERR_SHAPE;
     if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_SHAPE;
     // grid limit (65535 blocks of 64 tokens) and the 32-bit offsets of 19 rows
@@ -328,8 +331,17 @@ kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_
         misaligned(y))
         return KDA_ERR_ALIGN;
     const hipError_t e = kda::launch_short_conv(x, weight, cu_seqlens, num_seqs, total_tokens,
-                                                channels, conv_state, y, dtype == KDA_BF16, stream);
+                                                channels, conv_state, y, dtype == KDA_BF16,
+                                                l2norm_d, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_short_conv(const void *x, const float *weight, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_tokens, int32_t channels,
+                          float *conv_state, void *y, kda_dtype dtype, hipStream_t stream)
+{
+    return kda_short_conv_ex(x, weight, cu_seqlens, num_seqs, total_tokens, channels, conv_state,
+                             y, dtype, 0, stream);
 }
 
 kda_status kda_state_compose(const float *M, const float *S_in, const float *S_tilde,

@@ -272,7 +272,12 @@ __device__ __forceinline__ int seq_of(int64_t tok, const int32_t *__restrict__ c
 // Otherwise it slides a three-input window along the run, restarting it at
 // each sequence start from the streaming state or from zeros.  Either way
 // every input is read once per run, plus the three-row halo.
-template <typename T, int VEC, int RUN>
+// NORMD > 0: each row of NORMD channels (one head) of the output is then
+// L2-normalised (function table "L2Norm"; a zero row stays zero), so that the
+// layer's q = L2Norm(ShortConv(.)) needs no pass of its own.  The NORMD / VEC
+// lanes of a head are consecutive lanes of one wave, which all run the same
+// tokens, and reduce the sum of squares with xor shuffles.
+template <typename T, int VEC, int RUN, int NORMD>
 __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x,
                                                          const float *__restrict__ w,
                                                          const int32_t *__restrict__ cu,
@@ -283,6 +288,21 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x
 {
     typedef T vecT __attribute__((ext_vector_type(VEC)));
     typedef float vecF __attribute__((ext_vector_type(VEC)));
+    constexpr int LPH = NORMD / VEC;                 // lanes of a head (NORMD > 0)
+    static_assert(NORMD == 0 || (LPH >= 1 && LPH <= 64 && (LPH & (LPH - 1)) == 0), "head lanes");
+    // the output row of one token: L2-normalised over the head's lanes
+    const auto finish = [&](float (&o)[VEC]) __attribute__((always_inline)) {
+        if (NORMD > 0) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) ss += o[e] * o[e];
+#pragma unroll
+            for (int m = 1; m < LPH; m <<= 1) ss += __shfl_xor(ss, m);
+            const float r = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] *= r;
+        }
+    };
     const int ng = C / VEC;
     const int grp = blockIdx.x * 64 + (threadIdx.x & 63);
     if (grp >= ng) return;
@@ -312,11 +332,15 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x
             xs[j] = *reinterpret_cast<const vecT *>(xb + (uint32_t)j * rowb + cb);
 #pragma unroll
         for (int t = 0; t < RUN; ++t) {
-            vecT out;
+            float o[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                out[e] = from_f32<T>(wt[e][0] * to_f32(xs[t][e]) + wt[e][1] * to_f32(xs[t + 1][e]) +
-                                     wt[e][2] * to_f32(xs[t + 2][e]) + wt[e][3] * to_f32(xs[t + 3][e]));
+                o[e] = wt[e][0] * to_f32(xs[t][e]) + wt[e][1] * to_f32(xs[t + 1][e]) +
+                       wt[e][2] * to_f32(xs[t + 2][e]) + wt[e][3] * to_f32(xs[t + 3][e]);
+            finish(o);
+            vecT out;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) out[e] = from_f32<T>(o[e]);
             __builtin_nontemporal_store(out, reinterpret_cast<vecT *>(yb + (uint32_t)t * rowb + cb));
         }
         return;
@@ -357,11 +381,15 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x
         vecF cur;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) cur[e] = to_f32(xx[e]);
-        vecT out;
+        float o[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-            out[e] = from_f32<T>(wt[e][0] * win[0][e] + wt[e][1] * win[1][e] +
-                                 wt[e][2] * win[2][e] + wt[e][3] * cur[e]);
+            o[e] = wt[e][0] * win[0][e] + wt[e][1] * win[1][e] + wt[e][2] * win[2][e] +
+                   wt[e][3] * cur[e];
+        finish(o);
+        vecT out;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) out[e] = from_f32<T>(o[e]);
         *reinterpret_cast<vecT *>(y + t * C + c0) = out;
         win[0] = win[1];
         win[1] = win[2];
@@ -404,7 +432,7 @@ __global__ __launch_bounds__(256) void short_conv_state_kernel(const T *__restri
     }
 }
 
-template <typename T>
+template <typename T, int NORMD>
 static hipError_t launch_short_conv_t(const void *x, const float *w, const int32_t *cu, int nseq,
                                       int64_t ntok, int C, float *state, void *y,
                                       hipStream_t stream)
@@ -417,7 +445,7 @@ static hipError_t launch_short_conv_t(const void *x, const float *w, const int32
         // the fast path's 32-bit offsets: RUN + 3 rows of C elements
         if ((int64_t)(RUN + 3) * C * (int64_t)sizeof(T) >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
         const dim3 grid((unsigned)((C / VEC + 63) / 64), (unsigned)gy);
-        hipLaunchKernelGGL((short_conv_kernel<T, VEC, RUN>), grid, dim3(256), 0, stream,
+        hipLaunchKernelGGL((short_conv_kernel<T, VEC, RUN, NORMD>), grid, dim3(256), 0, stream,
                            (const T *)x, w, cu, nseq, seq_len, ntok, C, state, (T *)y);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -433,13 +461,30 @@ static hipError_t launch_short_conv_t(const void *x, const float *w, const int32
     return hipSuccess;
 }
 
+// normd: 0, or the head size over which each output row is L2-normalised.
+template <typename T>
+static hipError_t launch_short_conv_n(const void *x, const float *w, const int32_t *cu, int nseq,
+                                      int64_t ntok, int C, float *state, void *y, int normd,
+                                      hipStream_t stream)
+{
+#define KDA_SC_ARGS x, w, cu, nseq, ntok, C, state, y, stream
+    switch (normd) {
+        case 0: return launch_short_conv_t<T, 0>(KDA_SC_ARGS);
+        case 32: return launch_short_conv_t<T, 32>(KDA_SC_ARGS);
+        case 64: return launch_short_conv_t<T, 64>(KDA_SC_ARGS);
+        case 128: return launch_short_conv_t<T, 128>(KDA_SC_ARGS);
+    }
+#undef KDA_SC_ARGS
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, int nseq,
-                             int64_t ntok, int C, float *state, void *y, bool is_bf16,
+                             int64_t ntok, int C, float *state, void *y, bool is_bf16, int normd,
                              hipStream_t stream)
 {
     if (nseq == 0) return hipSuccess;
-    return is_bf16 ? launch_short_conv_t<bf16>(x, w, cu, nseq, ntok, C, state, y, stream)
-                   : launch_short_conv_t<float>(x, w, cu, nseq, ntok, C, state, y, stream);
+    return is_bf16 ? launch_short_conv_n<bf16>(x, w, cu, nseq, ntok, C, state, y, normd, stream)
+                   : launch_short_conv_n<float>(x, w, cu, nseq, ntok, C, state, y, normd, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -34,7 +34,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                             "kda_chunk_fwd_ex", "kda_output_gate_ex", "kda_chunk_fwd_algo",
                             "kda_chunk_fwd_algo_workspace_size", "kda_chunk_fwd_two_pass_static",
                             "kda_chunk_fwd_static_scratch_bytes", "kda_step_decode_gated", "kda_segment_scan",
-                            "kda_kcp_summaries", "kda_chunk_fwd_fused_ex", "kda_front_end"])
+                            "kda_kcp_summaries", "kda_chunk_fwd_fused_ex", "kda_front_end",
+                            "kda_short_conv_ex"])
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -330,6 +331,10 @@ def test_layer_steps_reject():
     assert lib.kda_state_compose(p(A), None, p(A), p(A), 4, 64, 64, None) == ENULL
     assert lib.kda_state_compose(p(A), p(A), p(A), p(MIS), 4, 64, 64, None) == EALIGN
     assert lib.kda_state_compose(None, None, None, None, 0, 64, 64, None) == OK
+    # ShortConv with the L2Norm of each head's row
+    sc = lambda nd, C=256: lib.kda_short_conv_ex(p(A), p(A), None, 1, 16, C, None, p(A), 1, nd, None)
+    assert sc(48) == EUNSUP and sc(128, C=192) == EUNSUP and sc(-1) == EUNSUP
+    assert lib.kda_short_conv_ex(p(A), p(A), None, 0, 0, 256, None, p(A), 1, 64, None) == OK
     # front end as a pass of its own
     fe = lambda **kw: (lambda a: lib.kda_front_end(
         a["qr"], a["kr"], a["z"], a["A"], a["b"], a["n"], 2, a["d"], a["dt"], a["q"], a["k"], a["g"],

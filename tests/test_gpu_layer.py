@@ -208,6 +208,42 @@ def test_short_conv_prefill(dtype, with_state, C):
         np.testing.assert_array_equal(_np(st), st_ref)    # copies of inputs: exact
 
 
+@pytest.mark.parametrize("dtype,d,H,with_state", [(torch.bfloat16, 128, 3, True),
+                                                  (torch.bfloat16, 64, 5, False),
+                                                  (torch.bfloat16, 32, 3, True),
+                                                  (torch.float32, 128, 2, True),
+                                                  (torch.float32, 32, 4, False)])
+def test_short_conv_l2norm(dtype, d, H, with_state):
+    """ShortConv then L2Norm of each head's row in one pass, against the
+    oracle's two steps; the state update is the plain ShortConv's."""
+    gen = torch.Generator(device=dev).manual_seed(5 + d)
+    lens = [5, 0, 1, 2, 300, 64, 17]
+    n, C = sum(lens), H * d
+    x = torch.randn(n, C, generator=gen, device=dev).to(dtype)
+    x[40, :d] = 0                       # a zero input row of one head ...
+    w = torch.randn(C, 4, generator=gen, device=dev)
+    w[:d, 3] = 0                        # ... whose three earlier inputs stay
+    x[37:40, :d] = 0                    # zero, so its output row is zero
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    st = torch.randn(len(lens), 3, C, generator=gen, device=dev) if with_state else None
+    st_in = None if st is None else _np(st)
+    st2 = None if st is None else st.clone()
+    y = kda.short_conv(x, w, cu_seqlens=cu, conv_state=st, l2norm_d=d)
+    kda.short_conv(x, w, cu_seqlens=cu, conv_state=st2)
+    torch.cuda.synchronize()
+    yc, st_ref = L.short_conv(_np(x), _np(w), cu_seqlens=cu.cpu().numpy(), conv_state=st_in)
+    y_ref = L.l2norm(yc.reshape(n, H, d)).reshape(n, C)
+    assert torch.count_nonzero(y[40, :d]) == 0
+    # one rounding of a unit row's entries
+    tol = 2 ** -8 if dtype == torch.bfloat16 else 2e-6
+    e = float(np.max(np.abs(_np(y) - y_ref)))
+    print(f"[parity] short conv + L2Norm {dtype} d={d} state={with_state}: {e:.3e}", flush=True)
+    assert e <= tol
+    if with_state:
+        assert torch.equal(st, st2)
+        np.testing.assert_array_equal(_np(st), st_ref)
+
+
 def test_short_conv_decode_steps_equal_prefill():
     gen = torch.Generator(device=dev).manual_seed(4)
     N, T, C = 8, 6, 64
