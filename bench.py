@@ -217,9 +217,12 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
         "fused_ms": res["prefill_fused_prologue"]["ms_per_step"],
         "unfused_ms": ms_un, "split_ms": ms_sp,
         "pass_l2norm_gate": {"ms": ms_fe, "GB/s": _gbs(feb, ms_fe), "bytes_per_launch": feb,
-                             "frac": _gbs(feb, ms_fe) / HBM_PEAK_GBS},
+                             "frac": _gbs(feb, ms_fe) / HBM_PEAK_GBS,
+                             "traffic": _traffic("kda_layer.hip", "front_end_k3_8k")},
         "pass_l2norm": {"ms": ms_fn, "GB/s": _gbs(fnb, ms_fn), "bytes_per_launch": fnb,
-                        "frac": _gbs(fnb, ms_fn) / HBM_PEAK_GBS},
+                        "frac": _gbs(fnb, ms_fn) / HBM_PEAK_GBS,
+                        "traffic": _traffic("kda_layer.hip", "front_end_l2norm_k3_8k")},
+        "gate_fused_prefill_traffic": _traffic("kda_prefill.hip", "k3_prefill_8k_gate_fused"),
         "kernel": "kda::front_end_kernel"}
     del qn, kn, gn, of, sff
     # the prefill with its attention output in fp32 (kda_chunk_fwd_ex)
@@ -291,6 +294,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
     res["short_conv_l2norm"] = {"tokens": n_tok, "streams": 3, "separate_ms": ms_cs,
                                 "fused_ms": ms_cf,
                                 "fused_GB/s": _gbs(3 * cb, ms_cf),
+                                "traffic_per_normalising_launch": _traffic("kda_layer.hip",
+                                                                           "short_conv_l2norm_k3_8k"),
                                 "kernel": "kda::short_conv_kernel<..., NORMD = d_k>"}
     del xs, ys, qn, kn, sts
     del li, o, og, xc, st
@@ -329,7 +334,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                       "scan": {"roofline": {"bound": "hbm", "achieved": _gbs(sb, ms_scan),
                                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                             "frac": _gbs(sb, ms_scan) / HBM_PEAK_GBS,
-                                            "traffic": None, "kernel": "kda::scan_kernel",
+                                            "traffic": _traffic("kda_layer.hip", "kcp_scan_k3_8k"),
+                                            "kernel": "kda::scan_kernel",
                                             "bytes_per_launch": sb}}}
         cnt = w.H
         out = torch.empty_like(St[0])

@@ -576,7 +576,15 @@ __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ M,
 
     const int lane = threadIdx.x & 63, n16 = lane & 15, grp = lane >> 4;
     const int w = threadIdx.x >> 6;
-    const int h = blockIdx.x / NCB, c0 = (blockIdx.x % NCB) * CB;
+    // block b runs on XCD b mod 8: when H divides by 8, the NCB column blocks of
+    // a head are given blocks of one XCD, so that M[r] comes from HBM once and
+    // from that XCD's L2 for the other column blocks
+    int item = blockIdx.x;
+    if (H % 8 == 0) {
+        const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
+        item = (x * (H / 8) + slot / NCB) * NCB + slot % NCB;
+    }
+    const int h = item / NCB, c0 = (item % NCB) * CB;
     const int64_t DD = (int64_t)D * D;
     // block copies: thread t moves 4 consecutive columns of rows t / 8 + 32 j
     const int cr = threadIdx.x >> 3, cc = (threadIdx.x & 7) * 4;
