@@ -355,7 +355,11 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                                                 None, xn["cu_seqlens"], out=on, final_state=sfn),
                           args.steps, args.warmup, torch)
     nb = prefill_bytes(nt, ns, wn.H, wn.dk, wn.dv, e, e, False, True)
+    ms_g = graph_time(lambda: kda.chunk_fwd(xn["q"], xn["k"], xn["v"], xn["g"], xn["beta"], None,
+                                            xn["cu_seqlens"], out=on, final_state=sfn),
+                      args.steps, min(args.warmup, 5), torch)
     res["nano_k3_prefill"] = {"workload": wn.name, "tokens": nt, "ms_per_step": ms,
+                              "graph_ms_per_step": ms_g,
                               "tokens/s": nt / (ms * 1e-3),
                               "roofline": {"bound": "hbm", "achieved": _gbs(nb, ms),
                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -370,7 +374,11 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
     ms, _ = time_launches(lambda: kda.step_decode(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"],
                                                   xd["state"], out=od), args.steps, args.warmup, torch)
     db = decode_bytes(wd.decode_requests, wd.H, wd.dk, wd.dv, e, e)
+    ms_g = graph_time(lambda: kda.step_decode(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"],
+                                              xd["state"], out=od), args.steps, min(args.warmup, 5),
+                      torch)
     res["nano_k3_decode"] = {"workload": wd.name, "ms_per_step": ms, "GB/s": _gbs(db, ms),
+                             "graph_ms_per_step": ms_g, "graph_GB/s": _gbs(db, ms_g),
                              "roofline": {"bound": "hbm", "achieved": _gbs(db, ms),
                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                           "frac": _gbs(db, ms) / HBM_PEAK_GBS,
@@ -414,6 +422,25 @@ def time_launches(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) / steps, wall
+
+
+def graph_time(fn, steps, warmup, torch, per_graph=10):
+    """Average duration of `fn` replayed from a captured HIP graph of `per_graph`
+    calls (the binding launches on the current stream, which capture records):
+    the device's pace without the Python binding's per-call host work."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    ms, _ = time_launches(g.replay, steps, warmup, torch)
+    del g
+    return ms / per_graph
 
 
 def cpu_model():
