@@ -342,7 +342,7 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
         out = torch.empty_like(St[0])
         ms_c, _ = time_launches(lambda: kda.state_compose(M[0], St[0], St[1], out=out),
                                 args.steps, args.warmup, torch)
-        res["kcp"]["compose"] = {"count": cnt, "ms": ms_c,
+        res["kcp"]["compose"] = {"count": cnt, "ms": ms_c, "kernel": "kda::scan_kernel (P = 1)",
                                  "TFLOP/s": 2 * d ** 3 * cnt / (ms_c * 1e-3) / 1e12,
                                  "GB/s": _gbs(4 * d * d * 4 * cnt, ms_c)}
         del M, St, out, S_in, S_fin, xs, os_, sfs

@@ -395,8 +395,8 @@ kda_status kda_short_conv_ex(const void *x, const float *weight, const int32_t *
  * S_tilde[b] is the segment's final state from S = 0.
  *
  *   M        [count][d_k][d_k]     S_in, S_tilde, S_out   [count][d_k][d_v]
- * d_k == d_v in {32, 64, 128}.  S_out must not alias M or S_in; it may alias
- * S_tilde.
+ * d_k == d_v in {32, 64, 128}.  S_out may alias S_in or S_tilde, not M.
+ * It runs as one step of kda_segment_scan (P = 1, the batch as its heads).
  */
 kda_status kda_state_compose(const float *M, const float *S_in, const float *S_tilde,
                              float *S_out, int64_t count, int32_t d_k, int32_t d_v,

@@ -36,8 +36,6 @@ hipError_t launch_output_gate(const void *o_raw, const void *gate, const float *
 hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, int nseq,
                              int64_t ntok, int C, float *state, void *y, bool is_bf16, int normd,
                              hipStream_t stream);
-hipError_t launch_compose(const float *M, const float *S_in, const float *S_tilde, float *S_out,
-                          int64_t count, int d, hipStream_t stream);
 hipError_t launch_scan(const float *M, const float *St, const float *S0, float *S_in,
                        float *S_fin, int P, int H, int d, hipStream_t stream);
 hipError_t launch_kcp_summaries(const void *k, const void *v, const float *g, const float *beta,
@@ -354,7 +352,11 @@ kda_status kda_state_compose(const float *M, const float *S_in, const float *S_t
     if (!M || !S_in || !S_tilde || !S_out) return KDA_ERR_NULL;
     if (misaligned(M) || misaligned(S_in) || misaligned(S_tilde) || misaligned(S_out))
         return KDA_ERR_ALIGN;
-    const hipError_t e = kda::launch_compose(M, S_in, S_tilde, S_out, count, d_k, stream);
+    // one step of the segment scan (P = 1, the batch as heads): each workgroup
+    // reads its blocks of S_in and S~ before it writes that block of S_out
+    if (count * (d_k / 32) > INT32_MAX) return KDA_ERR_SHAPE;
+    const hipError_t e = kda::launch_scan(M, S_tilde, S_in, nullptr, S_out, 1, (int)count, d_k,
+                                          stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -9,12 +9,12 @@
 //   - the front end, unfused: L2Norm of q and k and the bounded gate
 //     ("Glossaire", entry "Decroissance bornee"; function table "L2Norm");
 //   - state composition for context-parallel segments: S_out = M S_in + S~
-//     ("Glossaire", entry "KCP"; notation table rows M_t and S~), one step
-//     over a batch, or the whole scan over P segments in one launch.
+//     ("Glossaire", entry "KCP"; notation table rows M_t and S~), the whole
+//     scan over P segments in one launch (one step over a batch is P = 1).
 // The first three are elementwise and bound by HBM bandwidth: coalesced
 // accesses (16-byte lanes for the gate and the front end, 8-byte for
 // ShortConv), fp32 arithmetic.  The
-// composition is a batch of dense fp32 products on the matrix cores
+// composition is a chain of dense fp32 products on the matrix cores
 // (v_mfma_f32_16x16x4_f32).
 #include "kda_common.hpp"
 
@@ -485,71 +485,6 @@ hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, i
     if (nseq == 0) return hipSuccess;
     return is_bf16 ? launch_short_conv_n<bf16>(x, w, cu, nseq, ntok, C, state, y, normd, stream)
                    : launch_short_conv_n<float>(x, w, cu, nseq, ntok, C, state, y, normd, stream);
-}
-
-// ---------------------------------------------------------------------------
-// State composition S_out[b] = M[b] S_in[b] + S~[b], fp32.  A wave computes a
-// 16-row strip by 64 columns (four 16 x 16 tiles) of one product, K = DK in
-// steps of 4: lane (n16, grp) supplies M[row n16][k + grp] and
-// S_in[k + grp][column n16] to v_mfma_f32_16x16x4_f32 and ends with
-// D[4 grp + i][n16].
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void compose_kernel(const float *__restrict__ M,
-                                                      const float *__restrict__ S_in,
-                                                      const float *S_tilde, float *S_out,
-                                                      int64_t count)
-{
-    constexpr int NRS = DK / 16;                    // row strips
-    constexpr int NCB = (DV + 63) / 64;             // 64-column blocks
-    constexpr int NCT = (DV < 64 ? DV : 64) / 16;   // 16-column tiles per block
-    const int lane = threadIdx.x & 63, n16 = lane & 15, grp = lane >> 4;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t b = wave / (NRS * NCB);
-    if (b >= count) return;
-    const int rs = (int)((wave / NCB) % NRS), cb = (int)(wave % NCB);
-    const float *Mb = M + b * DK * DK;
-    const float *Sb = S_in + b * DK * DV;
-    f32x4 acc[NCT];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) acc[j] = zero4();
-#pragma unroll 4
-    for (int k = 0; k < DK; k += 4) {
-        const float a = Mb[(16 * rs + n16) * DK + k + grp];
-#pragma unroll
-        for (int j = 0; j < NCT; ++j)
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                a, Sb[(k + grp) * DV + 64 * cb + 16 * j + n16], acc[j], 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t off = b * DK * DV + (int64_t)(16 * rs + 4 * grp + i) * DV + 64 * cb + 16 * j + n16;
-            S_out[off] = acc[j][i] + S_tilde[off];
-        }
-}
-
-template <int D>
-static hipError_t launch_compose_t(const float *M, const float *S_in, const float *S_tilde,
-                                   float *S_out, int64_t count, hipStream_t stream)
-{
-    constexpr int NRS = D / 16, NCB = (D + 63) / 64;
-    const int64_t waves = count * NRS * NCB;
-    hipLaunchKernelGGL((compose_kernel<D, D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                       stream, M, S_in, S_tilde, S_out, count);
-    return hipGetLastError();
-}
-
-hipError_t launch_compose(const float *M, const float *S_in, const float *S_tilde, float *S_out,
-                          int64_t count, int d, hipStream_t stream)
-{
-    if (count == 0) return hipSuccess;
-    switch (d) {
-        case 32: return launch_compose_t<32>(M, S_in, S_tilde, S_out, count, stream);
-        case 64: return launch_compose_t<64>(M, S_in, S_tilde, S_out, count, stream);
-        case 128: return launch_compose_t<128>(M, S_in, S_tilde, S_out, count, stream);
-    }
-    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

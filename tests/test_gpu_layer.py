@@ -272,6 +272,12 @@ def test_state_compose(d):
     e = _rel(_np(out), ref)
     print(f"[parity] state compose d={d}: {e:.3e}")
     assert e <= 1e-5
+    # in place on S_in, and on S_tilde: the same result
+    S2, St2 = S.clone(), St.clone()
+    kda.state_compose(M, S2, St, out=S2)
+    kda.state_compose(M, S, St2, out=St2)
+    torch.cuda.synchronize()
+    assert torch.equal(S2, out) and torch.equal(St2, out)
 
 
 @pytest.mark.parametrize("d,P,H,with_s0", [(32, 5, 3, True), (64, 1, 2, False), (128, 8, 4, True),
