@@ -243,11 +243,16 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                      "frac": _gbs(pb, ms) / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "kda::prefill_kernel<..., fp32 o>", "bytes_per_launch": pb}}
     del o32, sf32
-    # output epilogue on the prefill's output rows
+    # output epilogue on the prefill's output rows.  Each launch takes the next
+    # of three input sets and writes the next of three outputs (1.8 GB in all),
+    # so that no launch reads what the previous one left in the 256 MB
+    # Infinity Cache: the figure is HBM's
     rows = n_tok * w.H
-    og = torch.empty_like(o)
-    ms, _ = time_launches(lambda: kda.output_gate(o, li["gate"], li["rms_weight"], out=og),
-                          args.steps, args.warmup, torch)
+    og_sets = [(o, li["gate"]), (li["q_raw"], li["k_raw"]), (li["z"], x["q"])]
+    ogs = [torch.empty_like(o) for _ in range(3)]
+    ms, _ = time_launches(cycled([lambda i=i: kda.output_gate(og_sets[i][0], og_sets[i][1],
+                                                              li["rms_weight"], out=ogs[i])
+                                  for i in range(3)]), args.steps, args.warmup, torch)
     ob = rows * w.dv * 3 * e + 4 * w.dv
     res["output_gate"] = {"rows": rows, "d_v": w.dv, "ms_per_step": ms, "GB/s": _gbs(ob, ms),
                           "roofline": {"bound": "hbm", "achieved": _gbs(ob, ms),
@@ -256,11 +261,15 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                                        "traffic": _traffic("kda_layer.hip", "output_gate_k3_8k"),
                                        "kernel": "kda::output_gate_kernel",
                                        "bytes_per_launch": ob}}
-    # ShortConv over one projection (H * d_k channels), with streaming state
-    xc = li["k_raw"].view(n_tok, w.H * w.dk)
-    st = torch.zeros(n_seq, 3, w.H * w.dk, device=dev)
-    ms, _ = time_launches(lambda: kda.short_conv(xc, li["conv_w"], x["cu_seqlens"], st),
-                          args.steps, args.warmup, torch)
+    # ShortConv over one projection (H * d_k channels), with streaming state;
+    # the launches cycle over three projections and outputs, as above
+    C3 = w.H * w.dk
+    xcs = [li["q_raw"].view(n_tok, C3), li["k_raw"].view(n_tok, C3), x["v"].view(n_tok, C3)]
+    ycs = [torch.empty_like(xcs[0]) for _ in range(3)]
+    st = torch.zeros(n_seq, 3, C3, device=dev)
+    ms, _ = time_launches(cycled([lambda i=i: kda.short_conv(xcs[i], li["conv_w"], x["cu_seqlens"],
+                                                             st, out=ycs[i])
+                                  for i in range(3)]), args.steps, args.warmup, torch)
     cb = n_tok * w.H * w.dk * 2 * e + w.H * w.dk * 16 + n_seq * 3 * w.H * w.dk * 8
     res["short_conv"] = {"tokens": n_tok, "channels": w.H * w.dk, "ms_per_step": ms,
                          "GB/s": _gbs(cb, ms),
@@ -273,7 +282,6 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
     # the layer's q, k, v from their projections: ShortConv of each, then a
     # pass for the L2Norm of q and k ("separate"), against ShortConv with the
     # L2Norm in the same pass for q and k ("fused")
-    C3 = w.H * w.dk
     xs = [li["q_raw"].view(n_tok, C3), li["k_raw"].view(n_tok, C3), x["v"].view(n_tok, C3)]
     ys = [torch.empty_like(xs[0]) for _ in range(3)]
     qn, kn = torch.empty_like(ys[0]), torch.empty_like(ys[1])
@@ -299,7 +307,7 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
                                                                            "short_conv_l2norm_k3_8k"),
                                 "kernel": "kda::short_conv_kernel<..., NORMD = d_k>"}
     del xs, ys, qn, kn, sts
-    del li, o, og, xc, st
+    del li, o, ogs, og_sets, xcs, ycs, st
     # context-parallel segments: the sequence split in P = 4 ("Glossaire",
     # entry "KCP").  Each of P devices would compute its segment's summaries,
     # take part in the scan and run its segment's prefill from the state the
@@ -423,6 +431,16 @@ def time_launches(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) / steps, wall
+
+
+def cycled(fns):
+    """A callable that runs fns[0], fns[1], ... in turn, one per call."""
+    state = {"i": 0}
+
+    def call():
+        fns[state["i"] % len(fns)]()
+        state["i"] += 1
+    return call
 
 
 def graph_time(fn, steps, warmup, torch, per_graph=10):

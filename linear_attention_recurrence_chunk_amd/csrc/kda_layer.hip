@@ -296,8 +296,14 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T *__restrict__ x
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) ss += o[e] * o[e];
+            if (LPH >= 16) {
+                // within a row of 16 lanes with DPP moves, then across rows
+                ss = row16_sum(ss);
+                if (LPH == 32) ss += __shfl_xor(ss, 16);
+            } else {
 #pragma unroll
-            for (int m = 1; m < LPH; m <<= 1) ss += __shfl_xor(ss, m);
+                for (int m = 1; m < LPH; m <<= 1) ss += __shfl_xor(ss, m);
+            }
             const float r = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) o[e] *= r;

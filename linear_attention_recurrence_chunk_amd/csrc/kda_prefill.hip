@@ -420,17 +420,6 @@ __device__ __forceinline__ void gate_items(const Smem<T, DK, BV> &sm, ChunkRegs<
         for (int cc = 0; cc < 2; ++cc) R.g[r][cc] = bounded_alpha(to_f32(R.z[r][cc]), gc.eA, b2[cc]);
 }
 
-// Sum over the 16 lanes of a row of the wave (lanes 16 j .. 16 j + 15), with
-// DPP moves: swap neighbours, swap pairs, then rotate the row by 4 and by 8.
-__device__ __forceinline__ float row16_sum(float x)
-{
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
-    return x;
-}
-
 // Fused prologue: partial sums of squares of the raw k and q rows of this
 // thread's item, over the wave's 32 channels; lane 0 of each row quarter
 // stores them for the elementwise phase, which adds the WPB partials of a row.
