@@ -17,7 +17,8 @@
 // therefore reads whole rows, fully coalesced, and keeps its share of S in
 // registers between the read and the write.  The next item's state is loaded
 // while the current one is finished, so that every wave always has a state
-// read in flight.  At d = 128 the wide workgroup keeps each thread's share of
+// read in flight.  The shared arrays come in two sets used by alternate items,
+// so that an item needs three barriers.  At d = 128 the wide workgroup keeps each thread's share of
 // the current and next state at 4 + 4 vectors (under 100 VGPRs instead of 204
 // with 256 threads), which lets more waves per SIMD stream: 6.1 TB/s against
 // 5.4.  The per-row partial sums of y and z are first added across the lanes
@@ -56,11 +57,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(const T *__restrict__ q,
     const int col = (t % TPR) * 4;
     const int r0 = t / TPR;
 
-    __shared__ float sq[DK], sk[DK], sa[DK];
+    // Shared arrays, two sets used by alternate items: a wave may start writing
+    // item i + 1's set while others still read item i's, and item i + 1's first
+    // barrier comes only after every wave has finished item i - 1, the last
+    // user of that set, so an item needs three barriers, not four.
     constexpr int NW = NT / 64;        // waves
-    __shared__ f32x4 ry[NW][TPR], rz[NW][TPR];
-    __shared__ float su[DV];
-    __shared__ float sqk;
+    __shared__ float sq[2][DK], sk[2][DK], sa[2][DK];
+    __shared__ f32x4 ry[2][NW][TPR], rz[2][NW][TPR];
+    __shared__ float su[2][DV];
+    __shared__ float sqk[2];
+    int pb = 0;
 
     int64_t nh = blockIdx.x;           // request * H + head
     f32x4 s[NPASS];
@@ -99,26 +105,26 @@ __global__ __launch_bounds__(NT) void decode_kernel(const T *__restrict__ q,
         }
 
         for (int c = t; c < DK; c += NT) {
-            sq[c] = to_f32(q[nh * DK + c]);
-            sk[c] = to_f32(k[nh * DK + c]);
-            sa[c] = __expf(g[nh * DK + c]);
+            sq[pb][c] = to_f32(q[nh * DK + c]);
+            sk[pb][c] = to_f32(k[nh * DK + c]);
+            sa[pb][c] = __expf(g[nh * DK + c]);
         }
         __syncthreads();
 
         if (t < 64) {  // q . k on wave 0
             float acc = 0.f;
-            for (int c = t; c < DK; c += 64) acc += sq[c] * sk[c];
+            for (int c = t; c < DK; c += 64) acc += sq[pb][c] * sk[pb][c];
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-            if (t == 0) sqk = acc;
+            if (t == 0) sqk[pb] = acc;
         }
 
         f32x4 y = zero4(), z = zero4();
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int c = r0 + p * RPP;
-            const float a = sa[c];
-            const float ka = sk[c] * a, qa = sq[c] * a;
+            const float a = sa[pb][c];
+            const float ka = sk[pb][c] * a, qa = sq[pb][c] * a;
             y += ka * s[p];
             z += qa * s[p];
         }
@@ -133,22 +139,22 @@ __global__ __launch_bounds__(NT) void decode_kernel(const T *__restrict__ q,
             }
         }
         if ((t & 63) < TPR) {
-            ry[t / 64][t & 63] = y;
-            rz[t / 64][t & 63] = z;
+            ry[pb][t / 64][t & 63] = y;
+            rz[pb][t / 64][t & 63] = z;
         }
         __syncthreads();
 
         if (t < TPR) {
             f32x4 yy = zero4(), zz = zero4();
 #pragma unroll
-            for (int r = 0; r < NW; ++r) { yy += ry[r][t]; zz += rz[r][t]; }
+            for (int r = 0; r < NW; ++r) { yy += ry[pb][r][t]; zz += rz[pb][r][t]; }
             const float b = vb;
-            const float qk = sqk;
+            const float qk = sqk[pb];
             float ov[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float u = b * (vv[i] - yy[i]);
-                su[col + i] = u;
+                su[pb][col + i] = u;
                 ov[i] = zz[i] + qk * u;
             }
             if (!GATED || o) {
@@ -172,17 +178,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(const T *__restrict__ q,
         }
         __syncthreads();
 
-        const f32x4 u4 = f32x4{su[col], su[col + 1], su[col + 2], su[col + 3]};
+        const f32x4 u4 = f32x4{su[pb][col], su[pb][col + 1], su[pb][col + 2], su[pb][col + 3]};
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int c = r0 + p * RPP;
-            const f32x4 ns = sa[c] * s[p] + sk[c] * u4;
+            const f32x4 ns = sa[pb][c] * s[p] + sk[pb][c] * u4;
             __builtin_nontemporal_store(
                 ns, reinterpret_cast<f32x4 *>(S + (int64_t)(r0 + p * RPP) * DV + col));
         }
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) s[p] = sn[p];
-        __syncthreads();   // the shared arrays are reused by the next item
+        pb ^= 1;
     }
 }
 
