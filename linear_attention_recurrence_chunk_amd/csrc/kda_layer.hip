@@ -499,7 +499,7 @@ hipError_t launch_short_conv(const void *x, const float *w, const int32_t *cu, i
 // The columns of S evolve independently, so one workgroup owns one head's
 // 32-column block for the whole scan and keeps it in LDS (d x 32 fp32, rows
 // padded to 36 floats so that the four K rows of a fragment read fall in
-// different banks).  Each step, wave w computes TPW 16 x 16 tiles of
+// different banks; two copies, read and written by alternate steps).  Each step, wave w computes TPW 16 x 16 tiles of
 // M[r] S + S~[r] on v_mfma_f32_16x16x4_f32; within a 16-wide K block, lane
 // group grp supplies K index kb + 4 grp + s at sub-step s to both operands, so
 // that its four M values are one 16-byte read.  M[r] and S~[r] are read once
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ M,
     constexpr int CB = 32, NCB = D / CB, NCT = CB / 16, LDW = CB + 4;
     constexpr int TILES = (D / 16) * NCT, TPW = TILES / 4;
     static_assert(TPW >= 1 && TILES % 4 == 0, "shape");
-    __shared__ float sS[D][LDW];
+    __shared__ float sS[2][D][LDW];    // the state entering step r is in sS[r & 1]
 
     const int lane = threadIdx.x & 63, n16 = lane & 15, grp = lane >> 4;
     const int w = threadIdx.x >> 6;
@@ -536,18 +536,22 @@ __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ M,
         if (S0)
             x = *reinterpret_cast<const f32x4 *>(S0 + h * DD + (int64_t)(cr + 32 * j) * D + c0 + cc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sS[cr + 32 * j][cc + i] = x[i];
+        for (int i = 0; i < 4; ++i) sS[0][cr + 32 * j][cc + i] = x[i];
     }
 
+    // one barrier a step: step r reads sS[r & 1] and writes sS[(r + 1) & 1],
+    // which step r - 1 finished reading before this step's barrier
     for (int r = 0; r < P; ++r) {
-        __syncthreads();   // S complete in LDS
+        __syncthreads();   // S complete in sS[r & 1]
+        const float(*cur)[LDW] = sS[r & 1];
+        float(*nxt)[LDW] = sS[(r + 1) & 1];
         const int64_t base = ((int64_t)r * H + h) * DD;
         if (S_in) {
 #pragma unroll
             for (int j = 0; j < D / 32; ++j) {
                 const int row = cr + 32 * j;
                 *reinterpret_cast<f32x4 *>(S_in + base + (int64_t)row * D + c0 + cc) =
-                    f32x4{sS[row][cc], sS[row][cc + 1], sS[row][cc + 2], sS[row][cc + 3]};
+                    f32x4{cur[row][cc], cur[row][cc + 1], cur[row][cc + 2], cur[row][cc + 3]};
             }
         }
         f32x4 acc[TPW];
@@ -569,23 +573,23 @@ __global__ __launch_bounds__(256) void scan_kernel(const float *__restrict__ M,
 #pragma unroll
                 for (int sub = 0; sub < 4; ++sub)
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        a[sub], sS[kb + 4 * grp + sub][16 * ct + n16], acc[t], 0, 0, 0);
+                        a[sub], cur[kb + 4 * grp + sub][16 * ct + n16], acc[t], 0, 0, 0);
             }
         }
-        __syncthreads();   // every read of S done
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int tile = w * TPW + t, rs = tile / NCT, ct = tile % NCT;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sS[16 * rs + 4 * grp + i][16 * ct + n16] = acc[t][i];
+            for (int i = 0; i < 4; ++i) nxt[16 * rs + 4 * grp + i][16 * ct + n16] = acc[t][i];
         }
     }
     __syncthreads();
+    const float(*fin)[LDW] = sS[P & 1];
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
         const int row = cr + 32 * j;
         *reinterpret_cast<f32x4 *>(S_fin + h * DD + (int64_t)row * D + c0 + cc) =
-            f32x4{sS[row][cc], sS[row][cc + 1], sS[row][cc + 2], sS[row][cc + 3]};
+            f32x4{fin[row][cc], fin[row][cc + 1], fin[row][cc + 2], fin[row][cc + 3]};
     }
 }
 
