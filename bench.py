@@ -109,7 +109,8 @@ def bench_configs(args, torch, kda, inputs, dev):
                       "ms_per_step": ms, "tokens/s": nt / (ms * 1e-3),
                       "roofline": {"bound": "hbm", "achieved": _gbs(b, ms), "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": _gbs(b, ms) / HBM_PEAK_GBS,
-                                   "traffic": None,
+                                   "traffic": _traffic("kda_chunked.hip" if two else "kda_prefill.hip",
+                                                       label),
                                    "kernel": ("kda::cp::intra_kernel + kda::cp::state_kernel"
                                               if two else "kda::prefill_kernel"),
                                    "bytes_per_launch": b},
@@ -240,7 +241,8 @@ def bench_layer(args, w, x, torch, kda, inputs, dev):
     res["prefill_fp32_output"] = {
         "workload": w.name, "ms_per_step": ms, "tokens/s": n_tok / (ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": _gbs(pb, ms), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": _gbs(pb, ms) / HBM_PEAK_GBS, "traffic": None,
+                     "frac": _gbs(pb, ms) / HBM_PEAK_GBS,
+                     "traffic": _traffic("kda_prefill.hip", "k3_prefill_8k_fp32_output"),
                      "kernel": "kda::prefill_kernel<..., fp32 o>", "bytes_per_launch": pb}}
     del o32, sf32
     # output epilogue on the prefill's output rows.  Each launch takes the next
